@@ -1,0 +1,281 @@
+/*
+ * CPU oracle for the emulated-FP32 GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no source, header, table or helper
+ * with the HIP library; the two meet only through seeded input arrays.
+ *
+ * The method it models is described on the NVIDIA technical blog page
+ * "Unlocking Tensor Core Performance for Machine Learning Interatomic
+ * Potentials" (cited below as [TC-MLIP]):
+ *   - section "How Tensor Core FP32 bridges the hardware gap", Figure 1:
+ *     every FP32 operand is split into three scaled BF16 pieces ("significand
+ *     bands"), the nine pairwise products are evaluated on the matrix unit and
+ *     accumulated in FP32 along five anti-diagonal bands, then recombined with
+ *     the required scaling;
+ *   - same section, Figure 2 and its equation a*b ~ a_hi*b_hi + a_hi*b_lo +
+ *     a_lo*b_hi: the three-product variant drops the smallest products;
+ *   - section "Limitations and decision criteria": against an FP64 reference,
+ *     BF16x9 matches or beats native FP32 accuracy.
+ *
+ * Where the page is silent (rounding mode of the split, the scale factors,
+ * which bands the 6- and 3-product variants keep, how alpha/beta are
+ * applied, non-finite inputs), each function below states the reading it
+ * implements.
+ *
+ * Plain, slow code on purpose: scalar loops, no blocking, no tricks.  Build
+ * with -ffp-contract=off so every float operation written here is one IEEE
+ * binary32 operation.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static uint32_t f2u(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
+static float u2f(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+static float bf16_value(uint16_t h) { return u2f((uint32_t)h << 16); }
+
+/*
+ * R(x): FP32 -> BF16, round to nearest with ties to even, saturating.
+ *
+ * Reading: the page names BF16 pieces but no rounding mode; round-to-nearest
+ * -even is the IEEE default.  A finite x whose rounding would overflow to
+ * infinity returns the largest finite BF16 of its sign instead, so every
+ * finite FP32 value keeps a finite leading piece.  NaN -> the quiet NaN
+ * 0x7FC0 with x's sign, +-inf -> +-inf.
+ *
+ * Written from the definition: find the two BF16 neighbours of |x| and keep
+ * the nearer one, comparing the two distances exactly in double precision.
+ */
+static uint16_t bf16_rne_sat(float x)
+{
+    uint32_t bits = f2u(x);
+    uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    uint32_t mag = bits & 0x7FFFFFFFu;
+    if (mag > 0x7F800000u) return (uint16_t)(sign | 0x7FC0u);
+    if (mag == 0x7F800000u) return (uint16_t)(sign | 0x7F80u);
+
+    uint32_t down = mag & 0xFFFF0000u;          /* BF16 neighbour toward zero */
+    if (down == mag) return (uint16_t)(sign | (down >> 16));
+    uint32_t up = down + 0x00010000u;           /* BF16 neighbour away from zero */
+
+    double xd = (double)u2f(mag);
+    double dd = (double)u2f(down);
+    double ud = (up == 0x7F800000u) ? ldexp(1.0, 128) : (double)u2f(up);
+    double dist_down = xd - dd;                 /* exact in double */
+    double dist_up = ud - xd;
+
+    uint32_t pick;
+    if (dist_down < dist_up)
+        pick = down;
+    else if (dist_up < dist_down)
+        pick = up;
+    else
+        pick = ((down >> 16) & 1u) ? up : down; /* tie: keep the even one */
+
+    if (pick == 0x7F800000u) pick = 0x7F7F0000u; /* saturate */
+    return (uint16_t)(sign | (pick >> 16));
+}
+
+void oracle_bf16_round(const float* x, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_rne_sat(x[i]);
+}
+
+/*
+ * Split of one FP32 value into three scaled BF16 pieces
+ * ([TC-MLIP], "How Tensor Core FP32 bridges the hardware gap", Figure 1:
+ * three scaled BF16 components per FP32 operand).
+ *
+ * Reading of "scaled": each piece is the rounded residual of the previous
+ * ones, lifted by 2^8 so that it is a full-range BF16 number:
+ *     hi   = R(a)
+ *     mid' = R(2^8 * (a - hi))
+ *     lo'  = 2^8 * (2^8 * (a - hi) - mid')
+ * so that a == hi + 2^-8 * mid' + 2^-16 * lo' holds exactly for every finite
+ * FP32 a (each subtraction and power-of-two scaling is exact; lo' has at most
+ * eight significant bits and is therefore a BF16 value).  Zero residuals are
+ * +0.  Reading for non-finite a: hi = R(a), mid' = lo' = +0.
+ */
+static void split_one(float a, uint16_t* hi, uint16_t* mid, uint16_t* lo)
+{
+    uint32_t mag = f2u(a) & 0x7FFFFFFFu;
+    uint16_t h = bf16_rne_sat(a);
+    if (mag >= 0x7F800000u) {
+        *hi = h;
+        *mid = 0;
+        *lo = 0;
+        return;
+    }
+    float r1 = a - bf16_value(h);     /* first residual */
+    float m = r1 * 256.0f;            /* lifted by 2^8 */
+    uint16_t md = bf16_rne_sat(m);
+    float q = m - bf16_value(md);     /* second residual (at the mid' scale) */
+    float l = q * 256.0f;             /* lifted by 2^8 again */
+    *hi = h;
+    *mid = md;
+    *lo = (uint16_t)(f2u(l) >> 16);
+}
+
+void oracle_split_bf16x3(const float* x, int64_t n, uint16_t* hi, uint16_t* mid, uint16_t* lo)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) split_one(x[i], &hi[i], &mid[i], &lo[i]);
+}
+
+/* Element (r, c) of op(X), where op(X) is rows x cols and X is row-major. */
+static float op_elem(const float* X, int64_t ld, int trans, int64_t r, int64_t c)
+{
+    return trans ? X[c * ld + r] : X[r * ld + c];
+}
+
+/*
+ * Reference GEMM with FP64 accumulation: the plain definition of the result
+ * that the page measures accuracy against ([TC-MLIP], "Limitations and
+ * decision criteria": matrix-multiplication tests against an FP64
+ * reference).  Row-major; op(A) is M x K, op(B) is K x N.
+ *     out[i][j] = alpha * sum_{k ascending} opA(i,k) * opB(k,j) + beta * C[i][j]
+ * Products of two FP32 values are exact in FP64.  C is not read when
+ * beta == 0 (BLAS convention).  out is M x N with leading dimension N.
+ */
+void oracle_gemm_f64(int transA, int transB, int64_t M, int64_t N, int64_t K, double alpha,
+                     const float* A, int64_t lda, const float* B, int64_t ldb, double beta,
+                     const float* C, int64_t ldc, double* out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        double* row = out + i * N;
+        for (int64_t j = 0; j < N; ++j) row[j] = 0.0;
+        if (!transB) {
+            /* k outer, j inner: every row[j] still sums over k ascending */
+            for (int64_t k = 0; k < K; ++k) {
+                double a = (double)op_elem(A, lda, transA, i, k);
+                const float* brow = B + k * ldb;
+                for (int64_t j = 0; j < N; ++j) row[j] += a * (double)brow[j];
+            }
+        } else {
+            for (int64_t j = 0; j < N; ++j) {
+                const float* bcol = B + j * ldb;  /* opB(k, j) = B[j][k] */
+                double s = 0.0;
+                for (int64_t k = 0; k < K; ++k) s += (double)op_elem(A, lda, transA, i, k) * (double)bcol[k];
+                row[j] = s;
+            }
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            double c = (beta != 0.0) ? beta * (double)C[i * ldc + j] : 0.0;
+            row[j] = alpha * row[j] + c;
+        }
+    }
+}
+
+/*
+ * Scalar model of the emulated GEMM ([TC-MLIP], Figure 1 and its text;
+ * Figure 2's equation for the reduced variant).
+ *
+ *   pieces:  a = a0 + 2^-8 a1 + 2^-16 a2 with (a0, a1, a2) = (hi, mid', lo')
+ *   bands:   S_j = sum over k ascending, and over (u, v) with u + v = j and
+ *            u ascending, of a_u(i,k) * b_v(k,j)
+ *   kept:    nbands = 5 (all nine products, "BF16X9"), 3 (u + v <= 2, six
+ *            products, "BF16X6"), 2 (u + v <= 1, three products, "BF16X3").
+ *            Reading: the reduced variants drop the smallest bands, as the
+ *            three-product rule of Figure 2 drops the smallest product.
+ *   recombine, smallest band first:
+ *            t = S_{n-1};  t = S_j + 2^-8 * t  for j = n-2 .. 0
+ *   epilogue: out = alpha * t + beta * C   (C not read when beta == 0)
+ *
+ * acc_f64 == 0: every band sum, the recombination and the epilogue are
+ * binary32 operations, one rounding each (the FP32 accumulation the page
+ * describes).  acc_f64 == 1: the same steps in binary64 (the "exact-band"
+ * variant used for identities; exact whenever the band sums fit in 53 bits).
+ * out_f32 (acc_f64 == 0) or out_f64 (acc_f64 == 1) is M x N, leading
+ * dimension N.
+ */
+void oracle_emu_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, int nbands,
+                     int acc_f64, float alpha, const float* A, int64_t lda, const float* B,
+                     int64_t ldb, float beta, const float* C, int64_t ldc, float* out_f32,
+                     double* out_f64)
+{
+    if (nbands < 1) nbands = 1;
+    if (nbands > 5) nbands = 5;
+
+    /* Pieces as float values: Ap[(i*K + k)*3 + u], Bp[(j*K + k)*3 + v]. */
+    float* Ap = (float*)malloc(sizeof(float) * 3 * (size_t)(M * K > 0 ? M * K : 1));
+    float* Bp = (float*)malloc(sizeof(float) * 3 * (size_t)(N * K > 0 ? N * K : 1));
+    if (!Ap || !Bp) {
+        free(Ap);
+        free(Bp);
+        abort();
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t h, m, l;
+            split_one(op_elem(A, lda, transA, i, k), &h, &m, &l);
+            float* p = Ap + (i * K + k) * 3;
+            p[0] = bf16_value(h);
+            p[1] = bf16_value(m);
+            p[2] = bf16_value(l);
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t h, m, l;
+            split_one(op_elem(B, ldb, transB, k, j), &h, &m, &l);
+            float* p = Bp + (j * K + k) * 3;
+            p[0] = bf16_value(h);
+            p[1] = bf16_value(m);
+            p[2] = bf16_value(l);
+        }
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            if (!acc_f64) {
+                float S[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+                for (int64_t k = 0; k < K; ++k) {
+                    const float* pa = Ap + (i * K + k) * 3;
+                    const float* pb = Bp + (j * K + k) * 3;
+                    for (int u = 0; u < 3; ++u)
+                        for (int v = 0; v < 3; ++v)
+                            if (u + v < nbands) S[u + v] += pa[u] * pb[v];
+                }
+                float t = S[nbands - 1];
+                for (int b = nbands - 2; b >= 0; --b) t = S[b] + 0.00390625f * t;
+                float r = alpha * t;
+                if (beta != 0.0f) r = r + beta * C[i * ldc + j];
+                out_f32[i * N + j] = r;
+            } else {
+                double S[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+                for (int64_t k = 0; k < K; ++k) {
+                    const float* pa = Ap + (i * K + k) * 3;
+                    const float* pb = Bp + (j * K + k) * 3;
+                    for (int u = 0; u < 3; ++u)
+                        for (int v = 0; v < 3; ++v)
+                            if (u + v < nbands) S[u + v] += (double)pa[u] * (double)pb[v];
+                }
+                double t = S[nbands - 1];
+                for (int b = nbands - 2; b >= 0; --b) t = S[b] + 0.00390625 * t;
+                double r = (double)alpha * t;
+                if (beta != 0.0f) r = r + (double)beta * (double)C[i * ldc + j];
+                out_f64[i * N + j] = r;
+            }
+        }
+    }
+    free(Ap);
+    free(Bp);
+}
+
+/* Number of threads the OpenMP runtime uses for the loops above. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
