@@ -1,0 +1,37 @@
+// Internal interface between the C-ABI layer (emu_api.hip) and the kernel
+// translation units.  Not installed; callers use include/emu_sgemm.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace emu {
+
+// One GEMM call after validation: row-major, op(A) M x K, op(B) K x N.
+struct GemmArgs {
+    bool trans_a, trans_b;
+    int64_t M, N, K;
+    float alpha, beta;
+    const float* A;
+    int64_t lda;
+    const float* B;
+    int64_t ldb;
+    float* C;
+    int64_t ldc;
+};
+
+struct DeviceInfo {
+    int num_cu;  // compute units of the current device
+};
+
+// nbands: 5 (BF16X9), 3 (BF16X6) or 2 (BF16X3).
+hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev,
+                            hipStream_t stream);
+hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, hipStream_t stream);
+// C = beta * C over M x N (zeroes C without reading it when beta == 0).
+hipError_t launch_scale_c(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
+                          hipStream_t stream);
+hipError_t launch_split(const float* x, int64_t n, uint16_t* hi, uint16_t* mid, uint16_t* lo,
+                        hipStream_t stream);
+
+}  // namespace emu

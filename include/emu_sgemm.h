@@ -1,0 +1,137 @@
+/*
+ * emu_sgemm -- FP32 GEMM emulated on bf16 MFMA matrix cores (AMD MI355X, gfx950).
+ *
+ * Method: "Unlocking Tensor Core Performance for Machine Learning Interatomic
+ * Potentials" (NVIDIA technical blog), section "How Tensor Core FP32 bridges
+ * the hardware gap":
+ *   - Figure 1: each FP32 operand is split into three scaled BF16 pieces; the
+ *     nine pairwise products run on the matrix unit and are accumulated in
+ *     FP32 along five anti-diagonal bands, then recombined with their scales.
+ *   - Figure 2 and its equation a*b ~ a_hi*b_hi + a_hi*b_lo + a_lo*b_hi: a
+ *     reduced variant keeps only the largest products.
+ * Section "BF16x9 on NVIDIA Blackwell GPUs" describes the SGEMM entry point
+ * (no model change) and the "performant" / "eager" policies; section "TF32x3
+ * on Ampere GPUs" describes the float-in / float-out linear layer whose
+ * forward GEMM and input-gradient GEMM dX = dY.W^T both use the emulation.
+ *
+ * Conventions (all entry points)
+ *   - Row-major storage.  op(A) is M x K, op(B) is K x N, C is M x N.
+ *       transA == EMU_OP_N: A stored M x K, lda >= max(1, K)
+ *       transA == EMU_OP_T: A stored K x M, lda >= max(1, M)
+ *       transB == EMU_OP_N: B stored K x N, ldb >= max(1, N)
+ *       transB == EMU_OP_T: B stored N x K, ldb >= max(1, K)
+ *       C stored M x N, ldc >= max(1, N)
+ *     A column-major caller computes C^T = B^T A^T by swapping operands.
+ *   - Every array pointer is device memory owned by the caller.  The library
+ *     keeps no reference to it after the call returns and allocates nothing.
+ *   - stream is a hipStream_t (NULL = the null stream).  Work is enqueued on
+ *     it asynchronously; errors during execution surface at the caller's
+ *     next synchronisation of that stream.
+ *   - Argument validation is synchronous and happens before any HIP call, so
+ *     an EMU_STATUS_INVALID_VALUE return has touched neither device nor stream.
+ *   - Re-entrant and thread-safe; calls on different streams may overlap.
+ */
+#ifndef EMU_SGEMM_H
+#define EMU_SGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { EMU_OP_N = 0, EMU_OP_T = 1 } emu_op_t;
+
+typedef enum {
+    /* FP32 MFMA (v_mfma_f32_32x32x2_f32): the native baseline. */
+    EMU_MODE_NATIVE_F32 = 0,
+    /* Nine products, five FP32 band accumulators (Figure 1). */
+    EMU_MODE_BF16X9 = 1,
+    /* Six products: bands 0..2 (piece-index sum u + v <= 2). */
+    EMU_MODE_BF16X6 = 2,
+    /* Three products hi*hi, hi*mid, mid*hi: bands 0..1 (Figure 2's rule). */
+    EMU_MODE_BF16X3 = 3,
+    /* Per-shape choice between NATIVE_F32 and BF16X9, the "performant"
+     * policy of section "BF16x9 on NVIDIA Blackwell GPUs". */
+    EMU_MODE_AUTO = 4
+} emu_mode_t;
+
+typedef enum {
+    EMU_STATUS_SUCCESS = 0,
+    EMU_STATUS_INVALID_VALUE = 1,  /* bad dimension, leading dimension, pointer or enum */
+    EMU_STATUS_NOT_SUPPORTED = 2,  /* no gfx950 device current, or device query failed */
+    EMU_STATUS_LAUNCH_FAILED = 3,  /* the kernel launch itself reported an error */
+    EMU_STATUS_ALLOC_FAILED = 4,   /* reserved: no entry point allocates */
+    EMU_STATUS_INTERNAL = 5
+} emu_status_t;
+
+/*
+ * C = alpha * op(A) . op(B) + beta * C in FP32, computed in `mode`.
+ *
+ * BF16X9/X6/X3: each element of op(A) and op(B) is split exactly into
+ * (hi, mid', lo') with hi = R(a), mid' = R(2^8 (a - hi)), lo' = 2^8 (2^8 (a -
+ * hi) - mid'), R = round to nearest even, saturating at the largest finite
+ * BF16 (Figure 1's "three scaled BF16 components").  Products with piece
+ * indices u + v = j are accumulated in FP32 band j; the bands kept (5, 3 or
+ * 2) are recombined smallest first, t = S_{n-1}, t = S_j + 2^-8 t, and then
+ * C = alpha * t + beta * C.
+ *
+ * Semantics follow BLAS SGEMM:
+ *   - M == 0 or N == 0: nothing is done.
+ *   - K == 0 or alpha == 0: C = beta * C (C is zeroed, not read, if beta == 0).
+ *   - beta == 0: C is written without being read (NaNs in C do not propagate).
+ * A or B overlapping C is undefined behaviour (not checked).  Any alignment
+ * and any leading dimension meeting the bounds above is accepted; 16-byte
+ * aligned pointers with leading dimensions that are multiples of 4 take the
+ * vectorised load path.  Non-finite inputs give non-finite outputs in
+ * NATIVE_F32, BF16X9 and BF16X6 (a NaN may appear where IEEE gives +-inf);
+ * BF16X3 propagates them too, but may overflow for finite inputs within
+ * 2^-15 of FLT_MAX.
+ *
+ * Errors: EMU_STATUS_INVALID_VALUE for M, N or K < 0, a leading dimension
+ * below its bound, a NULL A or B with M*N*K > 0, a NULL C with M*N > 0, or a
+ * transA/transB/mode outside its enum.  EMU_STATUS_NOT_SUPPORTED if the
+ * current device is not gfx950.  EMU_STATUS_LAUNCH_FAILED if the launch
+ * reports an error.
+ */
+emu_status_t emu_sgemm(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
+                       float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                       float beta, float* C, int64_t ldc, emu_mode_t mode, void* stream);
+
+/*
+ * The exact three-piece split on its own (Figure 1): for i < n,
+ *   hi[i], mid[i], lo[i] = BF16 bit patterns of hi, mid', lo' of x[i]
+ * with x[i] == hi + 2^-8 mid' + 2^-16 lo' exactly for every finite x[i].
+ * Non-finite x[i]: hi = +-inf (0x7F80 | sign) or the quiet NaN
+ * 0x7FC0 | sign, and mid' = lo' = +0.
+ * x: n floats; hi, mid, lo: n uint16 each; all device memory, any alignment.
+ * Errors: EMU_STATUS_INVALID_VALUE if n < 0 or a pointer is NULL with n > 0;
+ * EMU_STATUS_NOT_SUPPORTED / EMU_STATUS_LAUNCH_FAILED as for emu_sgemm.
+ */
+emu_status_t emu_split_bf16x3(const float* x, int64_t n, uint16_t* hi, uint16_t* mid,
+                              uint16_t* lo, void* stream);
+
+/*
+ * The mode EMU_MODE_AUTO runs for this shape: EMU_MODE_BF16X9 where the
+ * library's cost model predicts it faster than EMU_MODE_NATIVE_F32, else
+ * EMU_MODE_NATIVE_F32 (the "performant" policy; a caller who wants the
+ * "eager" policy passes EMU_MODE_BF16X9 directly).  A pure host function of
+ * (transA, transB, M, N, K): deterministic, no device access.
+ * Errors: EMU_STATUS_INVALID_VALUE for negative dimensions, a bad enum or a
+ * NULL `chosen`.
+ */
+emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N,
+                              int64_t K, emu_mode_t* chosen);
+
+/* Static, NUL-terminated name of a status code ("EMU_STATUS_..."); unknown
+ * codes give "EMU_STATUS_UNKNOWN".  Never NULL. */
+const char* emu_status_string(emu_status_t status);
+
+/* ABI version of this header (major * 100 + minor). */
+int emu_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EMU_SGEMM_H */

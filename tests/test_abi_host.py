@@ -1,0 +1,113 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no compute calls).
+
+The shared library must load, export every function declared in
+include/emu_sgemm.h, and reject invalid arguments with
+EMU_STATUS_INVALID_VALUE before making any HIP call.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+import emulated_fp32_matrix_amd as emu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "emu_sgemm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(emu_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert _declared_functions() == sorted(emu.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", emu.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (emu_[a-z0-9_]+)$", out, flags=re.M))
+    missing = set(_declared_functions()) - exported
+    assert not missing, missing
+
+
+def test_header_compiles_as_c():
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                   check=True)
+
+
+def test_status_strings_and_version():
+    assert emu.emu_status_string(0) == "EMU_STATUS_SUCCESS"
+    assert emu.emu_status_string(1) == "EMU_STATUS_INVALID_VALUE"
+    assert emu.emu_status_string(2) == "EMU_STATUS_NOT_SUPPORTED"
+    assert emu.emu_status_string(3) == "EMU_STATUS_LAUNCH_FAILED"
+    assert emu.emu_status_string(99) == "EMU_STATUS_UNKNOWN"
+    assert emu.emu_abi_version() == 100
+
+
+FAKE = 0x1000  # never dereferenced: validation fails (or returns) before any HIP call
+
+
+@pytest.mark.parametrize("args", [
+    dict(transA=2),
+    dict(transB=-1),
+    dict(mode=5),
+    dict(mode=-1),
+    dict(M=-1),
+    dict(N=-3),
+    dict(K=-1),
+    dict(lda=7),            # NN: lda >= K = 8
+    dict(transA=1, lda=9),  # TN: lda >= M = 10
+    dict(ldb=5),            # NN: ldb >= N = 6
+    dict(transB=1, ldb=7),  # NT: ldb >= K = 8
+    dict(ldc=5),            # ldc >= N = 6
+    dict(A=0),
+    dict(B=0),
+    dict(C=0),
+    dict(M=0, ldc=0),       # ld bounds hold for empty shapes too (ldc >= 1)
+])
+def test_invalid_arguments_rejected(args):
+    call = dict(transA=0, transB=0, M=10, N=6, K=8, alpha=1.0, A=FAKE, lda=8, B=FAKE, ldb=6,
+                beta=0.0, C=FAKE, ldc=6, mode=1, stream=0)
+    if args.get("transA") == 1 and "lda" not in args:
+        call["lda"] = 10
+    if args.get("transB") == 1 and "ldb" not in args:
+        call["ldb"] = 8
+    call.update(args)
+    assert emu.emu_sgemm(**call) == emu.STATUS_INVALID_VALUE
+
+
+def test_empty_shapes_return_before_touching_the_device():
+    base = dict(transA=0, transB=0, alpha=1.0, A=0, B=0, beta=0.0, C=0, mode=1, stream=0)
+    assert emu.emu_sgemm(M=0, N=5, K=4, lda=4, ldb=5, ldc=5, **base) == emu.STATUS_SUCCESS
+    assert emu.emu_sgemm(M=5, N=0, K=4, lda=4, ldb=1, ldc=1, **base) == emu.STATUS_SUCCESS
+    assert emu.emu_split_bf16x3(0, 0, 0, 0, 0, 0) == emu.STATUS_SUCCESS
+
+
+def test_split_invalid_arguments():
+    assert emu.emu_split_bf16x3(FAKE, -1, FAKE, FAKE, FAKE, 0) == emu.STATUS_INVALID_VALUE
+    for k in range(4):
+        ptrs = [FAKE] * 4
+        ptrs[k] = 0
+        assert emu.emu_split_bf16x3(ptrs[0], 16, ptrs[1], ptrs[2], ptrs[3], 0) == \
+            emu.STATUS_INVALID_VALUE
+
+
+def test_select_is_pure_and_deterministic():
+    st, _ = emu.emu_sgemm_select(0, 0, -1, 4, 4)
+    assert st == emu.STATUS_INVALID_VALUE
+    st, _ = emu.emu_sgemm_select(3, 0, 4, 4, 4)
+    assert st == emu.STATUS_INVALID_VALUE
+    shapes = [(552960, 768, 256), (6144, 256, 256), (64, 64, 8), (6144, 4096, 1024), (1, 1, 1),
+              (0, 5, 5)]
+    for M, N, K in shapes:
+        for ta in (0, 1):
+            for tb in (0, 1):
+                st, first = emu.emu_sgemm_select(ta, tb, M, N, K)
+                assert st == emu.STATUS_SUCCESS and first in ("BF16X9", "NATIVE_F32")
+                assert all(emu.emu_sgemm_select(ta, tb, M, N, K)[1] == first for _ in range(3))
+    # large MLIP shapes go to the emulation
+    assert emu.select_mode(552960, 768, 256) == "BF16X9"
