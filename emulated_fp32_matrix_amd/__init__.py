@@ -48,6 +48,13 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it first "
                       "(python -c 'import __graft_entry__ as g; g.build()')")
 
+# torch ships its own HIP runtime with the same soname (libamdhip64.so.7).
+# Loading torch first makes the library bind to that runtime, so the
+# process has one HIP runtime and torch's streams and allocations are valid
+# handles for the library; loading the library first would bring in a
+# second runtime from the ROCm installation.
+import torch as _torch_runtime  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p

@@ -84,7 +84,9 @@ emu_mode_t select_mode(int64_t M, int64_t N, int64_t K)
 
 emu_status_t from_hip(hipError_t e)
 {
-    return e == hipSuccess ? EMU_STATUS_SUCCESS : EMU_STATUS_LAUNCH_FAILED;
+    if (e == hipSuccess) return EMU_STATUS_SUCCESS;
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return EMU_STATUS_ALLOC_FAILED;
+    return EMU_STATUS_LAUNCH_FAILED;
 }
 
 }  // namespace

@@ -197,31 +197,234 @@ __device__ __forceinline__ void store_c_tile(const Params& p, const float (&t)[1
     }
 }
 
+// ---------------------------------------------------------------------------
+// Emulated GEMM, B operand pre-split.
+//
+// op(B) is split once per call by presplit_b_kernel into a workspace laid out
+// exactly as the kernel's LDS tiles: for every (n-tile, k-step) a chunk of NP
+// planes x 128 rows (n) x LDS_ROW bf16 (k, padded), rows past N and k past K
+// zero.  The GEMM kernel then copies each chunk to LDS with direct
+// global->LDS loads (no registers, no VALU, no bounds checks) and splits only
+// op(A), whose elements it loads, splits in registers and writes to LDS.
+// ---------------------------------------------------------------------------
+
+constexpr int WS_ROWS = 128;                         // n rows per B chunk (= BN)
+
+__host__ __device__ constexpr int64_t bchunk_elems(int np) { return (int64_t)np * WS_ROWS * LDS_ROW; }
+
+// One thread per (n, 8-wide k group) of the padded B extent.
+template <int NP>
+__global__ void presplit_b_kernel(const float* __restrict__ B, int64_t ldb, int trans_b, int64_t N,
+                                  int64_t K, int tiles_n, int nk, uint16_t* __restrict__ W)
+{
+    const int64_t npad = (int64_t)tiles_n * WS_ROWS;
+    const int64_t kgroups = (int64_t)nk * (BK / 8);
+    const int64_t total = npad * kgroups;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        int64_t n, kg;
+        if (trans_b) {  // B stored N x K: consecutive threads walk k
+            n = idx / kgroups;
+            kg = idx - n * kgroups;
+        } else {        // B stored K x N: consecutive threads walk n
+            kg = idx / npad;
+            n = idx - kg * npad;
+        }
+        const int64_t k0 = kg * 8;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t k = k0 + e;
+            v[e] = (n < N && k < K) ? (trans_b ? B[n * ldb + k] : B[k * ldb + n]) : 0.0f;
+        }
+        uint32_t h[4], m[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (NP == 3)
+                split_pair<true>(v[2 * e], v[2 * e + 1], h[e], m[e], l[e]);
+            else
+                split_pair_hm(v[2 * e], v[2 * e + 1], h[e], m[e]);
+        }
+        const int64_t tn = n / WS_ROWS, nn = n - tn * WS_ROWS;
+        const int64_t kt = k0 / BK, kk = k0 - kt * BK;
+        uint16_t* chunk = W + (tn * nk + kt) * bchunk_elems(NP);
+        const int64_t off = nn * LDS_ROW + kk;
+        *reinterpret_cast<u32x4_t*>(chunk + off) = u32x4_t{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<u32x4_t*>(chunk + WS_ROWS * LDS_ROW + off) = u32x4_t{m[0], m[1], m[2], m[3]};
+        if (NP == 3)
+            *reinterpret_cast<u32x4_t*>(chunk + 2 * WS_ROWS * LDS_ROW + off) =
+                u32x4_t{l[0], l[1], l[2], l[3]};
+    }
+}
+
+// Position in the static tile list plus k-step, advanced once per k-step.
+// next() saturates at the workgroup's last (tile, k-step), so prefetches past
+// the end re-read valid data instead of running off the operands.
+struct Cursor {
+    int tile, kt, tn;
+    int64_t m0;
+    __device__ __forceinline__ void set(const Params& p, int t, int bm)
+    {
+        tile = t;
+        kt = 0;
+        const int tm = t / p.tiles_n;
+        tn = t - tm * p.tiles_n;
+        m0 = (int64_t)tm * bm;
+    }
+    __device__ __forceinline__ void next(const Params& p, int G, int bm)
+    {
+        if (kt + 1 < p.nk) {
+            ++kt;
+        } else if (tile + G < p.ntiles) {
+            set(p, tile + G, bm);
+        }
+    }
+};
+
+// Per-thread element offsets of an op(A) tile (constant over the launch).
+template <bool KC, int ROWS, int RPP>
+struct APlan {
+    static constexpr int P = ROWS / RPP;
+    uint32_t off[P];   // offset of the thread's first element of row q
+    int row[P];        // row of the tile
+    int kk;            // first k of the thread's four
+    __device__ __forceinline__ void init(int64_t ld)
+    {
+        const int t = threadIdx.x;
+        kk = tile_k<KC, RPP>(t);
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            row[q] = tile_row<KC, RPP>(t, q);
+            off[q] = KC ? (uint32_t)(row[q] * ld + kk) : (uint32_t)(kk * ld + row[q]);
+        }
+    }
+};
+
+// Loads of a full tile (all rows < M, k0 + BK <= K): no checks.
+template <bool KC, int ROWS, int RPP>
+__device__ __forceinline__ void load_a_fast(RegTile<ROWS, RPP>& rt, const APlan<KC, ROWS, RPP>& pl,
+                                            const float* __restrict__ base, uint32_t ld, bool vec)
+{
+#pragma unroll
+    for (int q = 0; q < APlan<KC, ROWS, RPP>::P; ++q) {
+        if (KC && vec) {
+            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(base + pl.off[q]);
+            rt.v[q][0] = v[0];
+            rt.v[q][1] = v[1];
+            rt.v[q][2] = v[2];
+            rt.v[q][3] = v[3];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                rt.v[q][e] = base[pl.off[q] + (KC ? (uint32_t)e : (uint32_t)e * ld)];
+        }
+    }
+}
+
+// Loads of an edge tile: elements outside op(A) read as zero.
+template <bool KC, int ROWS, int RPP>
+__device__ __forceinline__ void load_a_edge(RegTile<ROWS, RPP>& rt, const APlan<KC, ROWS, RPP>& pl,
+                                            const float* __restrict__ base, uint32_t ld,
+                                            int64_t rows_left, int64_t k_left)
+{
+#pragma unroll
+    for (int q = 0; q < APlan<KC, ROWS, RPP>::P; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool ok = pl.row[q] < rows_left && pl.kk + e < k_left;
+            rt.v[q][e] = ok ? base[pl.off[q] + (KC ? (uint32_t)e : (uint32_t)e * ld)] : 0.0f;
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt
+    // (11:8) left at their maxima, i.e. not waited on.
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p)
+{
+    return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
+// Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at LDS
+// offset `lds_base + 16 l` (lds_base wave-uniform).  Written as inline
+// assembly so that the compiler does not guard every later LDS read with a
+// wait for this load; the caller waits (wait_vmcnt) before the barrier that
+// publishes the data.
+__device__ __forceinline__ const void* uniform_ptr(const void* p)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void copy16_to_lds(uint32_t lds_base, const void* gbase, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(uniform_ptr(gbase))
+                 : "memory");
+}
+
 // The emulated GEMM.  NB = bands kept: 5 (nine products), 3 (six), 2 (three).
-// Loop structure: for each tile of this workgroup, for each BK step of K:
-// MFMAs on the current LDS planes, then split the prefetched registers into
-// the other LDS buffer and prefetch the step after next (which may belong to
-// the next tile), one barrier per step; the epilogue follows a tile's last
-// step while the next tile's loads are in flight.
-template <class GEO, int NB, bool TA, bool TB>
-__global__ __launch_bounds__(GEO::NT, 1) void gemm_bf16_kernel(Params p)
+// Per k-step, in order: direct loads of the next B chunk into the other LDS
+// buffer; MFMAs on the current buffers interleaved with the split of the
+// prefetched A registers into the other buffer; loads of the A tile two steps
+// ahead; wait for the B chunk; one barrier.  The epilogue follows a tile's
+// last k-step while the next tile's loads are in flight.
+template <class GEO, int NB, bool TA>
+__global__ __launch_bounds__(GEO::NT, 1) void gemm_bf16_kernel(Params p, const uint16_t* __restrict__ W)
 {
     constexpr int BM = GEO::BM, BN = GEO::BN, TM = GEO::TM, TN = GEO::TN, RPP = GEO::RPP;
     constexpr int NP = NB >= 3 ? 3 : 2;  // planes used: hi, mid' (, lo')
     constexpr int PSA = BM * LDS_ROW, PSB = BN * LDS_ROW;
+    constexpr bool KC = !TA;             // op(A) k-contiguous in memory
+    static_assert(BN == WS_ROWS, "B chunk rows");
+    constexpr int CHUNK_BYTES = (int)(bchunk_elems(NP) * 2);
+    constexpr int COPY_ROUNDS = (CHUNK_BYTES + GEO::NT * 16 - 1) / (GEO::NT * 16);
+    constexpr int A_LOADS = KC ? RegTile<BM, RPP>::P : 4 * RegTile<BM, RPP>::P;
     __shared__ __attribute__((aligned(16))) uint16_t smA[2][NP * PSA];
     __shared__ __attribute__((aligned(16))) uint16_t smB[2][NP * PSB];
 
     const int G = gridDim.x;
     const int slot = xcd_position(blockIdx.x, G);
     const int my_tiles = (p.ntiles - slot + G - 1) / G;
-    const int total = my_tiles * p.nk;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / GEO::WN, wn = wave % GEO::WN;
     const int frag_row = lane & 31;
     const int frag_k = (lane >> 5) * 8;
+    const uint32_t lda = (uint32_t)p.lda;
+
+    APlan<KC, BM, RPP> plan;
+    plan.init(p.lda);
+
+    // Issue the direct loads of B chunk (tn, kt) into LDS buffer `buf`.
+    auto load_b = [&](const Cursor& c, int buf) {
+        const char* src = reinterpret_cast<const char*>(W + ((int64_t)c.tn * p.nk + c.kt) * bchunk_elems(NP));
+        const uint32_t dst = lds_offset(smB[buf]);
+#pragma unroll
+        for (int r = 0; r < COPY_ROUNDS; ++r) {
+            const int byte0 = (r * GEO::NT + wave * 64) * 16;  // this wave's 1 KB piece
+            if (byte0 < CHUNK_BYTES)
+                copy16_to_lds(dst + byte0, src + byte0, (uint32_t)lane * 16);
+        }
+    };
+    auto load_a = [&](RegTile<BM, RPP>& rt, const Cursor& c) {
+        const int64_t k0 = (int64_t)c.kt * BK;
+        const float* base = KC ? p.A + c.m0 * p.lda + k0 : p.A + k0 * p.lda + c.m0;
+        if (c.m0 + BM <= p.M && k0 + BK <= p.K)
+            load_a_fast<KC>(rt, plan, base, lda, p.vec_a != 0);
+        else
+            load_a_edge<KC>(rt, plan, base, lda, p.M - c.m0, p.K - k0);
+    };
 
     f32x16_t acc[TM][TN][NB];
 #pragma unroll
@@ -232,29 +435,24 @@ __global__ __launch_bounds__(GEO::NT, 1) void gemm_bf16_kernel(Params p)
             for (int b = 0; b < NB; ++b) acc[i][j][b] = f32x16_t{};
 
     RegTile<BM, RPP> ra;
-    RegTile<BN, RPP> rb;
-    // op(A) as [m][k]: k-contiguous unless A is transposed.
-    // op(B) as [n][k]: k-contiguous when B is transposed.
-    auto prefetch = [&](int it2) {
-        const int tl = it2 / p.nk;
-        const int kt = it2 - tl * p.nk;
-        int64_t m0, n0;
-        tile_coords(p, slot + tl * G, BM, BN, m0, n0);
-        const int64_t k0 = (int64_t)kt * BK;
-        load_tile<!TA>(ra, p.A, p.lda, p.M, p.K, m0, k0, p.vec_a);
-        load_tile<TB>(rb, p.B, p.ldb, p.N, p.K, n0, k0, p.vec_b);
-    };
-
-    prefetch(0);
-    store_tile_bf16<!TA, NP, PSA>(smA[0], ra);
-    store_tile_bf16<TB, NP, PSB>(smB[0], rb);
-    if (total > 1) prefetch(1);
+    Cursor cc, cb, ca;   // compute step it, B load step it+1, A load step it+2
+    cc.set(p, slot, BM);
+    cb = cc;
+    ca = cc;
+    load_b(cb, 0);
+    load_a(ra, ca);
+    store_tile_bf16<KC, NP, PSA>(smA[0], ra);
+    cb.next(p, G, BM);
+    ca.next(p, G, BM);
+    load_a(ra, ca);
+    ca.next(p, G, BM);
+    wait_vmcnt<A_LOADS>();
     __syncthreads();
 
-    int it = 0;
+    int cur = 0;
     for (int tl = 0; tl < my_tiles; ++tl) {
-        for (int kt = 0; kt < p.nk; ++kt, ++it) {
-            const int cur = it & 1;
+        for (int kt = 0; kt < p.nk; ++kt) {
+            load_b(cb, cur ^ 1);
             const uint16_t* As = smA[cur];
             const uint16_t* Bs = smB[cur];
 #pragma unroll
@@ -268,7 +466,6 @@ __global__ __launch_bounds__(GEO::NT, 1) void gemm_bf16_kernel(Params p)
                         bfr[pl][j] = *reinterpret_cast<const bf16x8_t*>(
                             Bs + pl * PSB + col * LDS_ROW + ks * 16 + frag_k);
                     }
-                // A planes from the smallest piece up; for each, every B piece.
 #pragma unroll
                 for (int u = NP - 1; u >= 0; --u) {
                     bf16x8_t af[TM];
@@ -291,17 +488,26 @@ __global__ __launch_bounds__(GEO::NT, 1) void gemm_bf16_kernel(Params p)
                     }
                 }
             }
-            if (it + 1 < total) {
-                store_tile_bf16<!TA, NP, PSA>(smA[cur ^ 1], ra);
-                store_tile_bf16<TB, NP, PSB>(smB[cur ^ 1], rb);
-                if (it + 2 < total) prefetch(it + 2);
+            // split of the prefetched A tile (step it+1) into the other buffer
+            store_tile_bf16<KC, NP, PSA>(smA[cur ^ 1], ra);
+            // Interleave the split's VALU work with the MFMAs of this step.
+            constexpr int N_MFMA = (BK / 16) * TM * TN * (NB == 5 ? 9 : NB == 3 ? 6 : 3);
+#pragma unroll
+            for (int g = 0; g < N_MFMA; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // then up to 3 VALU
             }
+            load_a(ra, ca);
+            cb.next(p, G, BM);
+            ca.next(p, G, BM);
+            wait_vmcnt<A_LOADS>();
             __syncthreads();
+            cur ^= 1;
         }
 
         // Epilogue: recombine the bands smallest first and store C.
-        int64_t cm0, cn0;
-        tile_coords(p, slot + tl * G, BM, BN, cm0, cn0);
+        const int64_t cm0 = cc.m0;
+        const int64_t cn0 = (int64_t)cc.tn * BN;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -319,6 +525,7 @@ __global__ __launch_bounds__(GEO::NT, 1) void gemm_bf16_kernel(Params p)
 #pragma unroll
                 for (int b = 0; b < NB; ++b) acc[i][j][b] = f32x16_t{};
             }
+        if (cc.tile + G < p.ntiles) cc.set(p, cc.tile + G, BM);
     }
 }
 
@@ -470,17 +677,13 @@ using GeoEmu = Geo<2, 4, 2, 1>;     // 8 waves, each 64x32: 128x128 per workgrou
 using GeoF32 = Geo<2, 2, 2, 2>;     // 4 waves, each 64x64: 128x128 per workgroup
 
 template <int NB>
-hipError_t launch_bands(const Params& p, bool ta, bool tb, int grid, hipStream_t s)
+hipError_t launch_bands(const Params& p, bool ta, int grid, const uint16_t* W, hipStream_t s)
 {
     constexpr int NT = GeoEmu::NT;
-    if (!ta && !tb)
-        hipLaunchKernelGGL((gemm_bf16_kernel<GeoEmu, NB, false, false>), dim3(grid), dim3(NT), 0, s, p);
-    else if (!ta && tb)
-        hipLaunchKernelGGL((gemm_bf16_kernel<GeoEmu, NB, false, true>), dim3(grid), dim3(NT), 0, s, p);
-    else if (ta && !tb)
-        hipLaunchKernelGGL((gemm_bf16_kernel<GeoEmu, NB, true, false>), dim3(grid), dim3(NT), 0, s, p);
+    if (!ta)
+        hipLaunchKernelGGL((gemm_bf16_kernel<GeoEmu, NB, false>), dim3(grid), dim3(NT), 0, s, p, W);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<GeoEmu, NB, true, true>), dim3(grid), dim3(NT), 0, s, p);
+        hipLaunchKernelGGL((gemm_bf16_kernel<GeoEmu, NB, true>), dim3(grid), dim3(NT), 0, s, p, W);
     return hipGetLastError();
 }
 
@@ -489,15 +692,36 @@ hipError_t launch_bands(const Params& p, bool ta, bool tb, int grid, hipStream_t
 hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev,
                             hipStream_t stream)
 {
+    if (nbands != 5 && nbands != 3 && nbands != 2) return hipErrorInvalidValue;
     if (!fits_32bit(g, GeoEmu::BM, GeoEmu::BN)) return hipErrorInvalidValue;
     const Params p = make_params(g, GeoEmu::BM, GeoEmu::BN);
-    const int grid = p.ntiles < dev.num_cu ? p.ntiles : dev.num_cu;
-    switch (nbands) {
-    case 5: return launch_bands<5>(p, g.trans_a, g.trans_b, grid, stream);
-    case 3: return launch_bands<3>(p, g.trans_a, g.trans_b, grid, stream);
-    case 2: return launch_bands<2>(p, g.trans_a, g.trans_b, grid, stream);
-    default: return hipErrorInvalidValue;
+    const int np = nbands >= 3 ? 3 : 2;
+    const size_t ws_bytes = (size_t)p.tiles_n * p.nk * bchunk_elems(np) * sizeof(uint16_t);
+    uint16_t* W = nullptr;
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&W), ws_bytes, stream);
+    if (e != hipSuccess) return hipErrorOutOfMemory;
+
+    const int64_t work = (int64_t)p.tiles_n * WS_ROWS * p.nk * (BK / 8);
+    int64_t blocks = (work + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    const int tb = g.trans_b ? 1 : 0;
+    if (np == 3)
+        hipLaunchKernelGGL(presplit_b_kernel<3>, dim3((unsigned)blocks), dim3(256), 0, stream, g.B,
+                           g.ldb, tb, g.N, g.K, p.tiles_n, p.nk, W);
+    else
+        hipLaunchKernelGGL(presplit_b_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, g.B,
+                           g.ldb, tb, g.N, g.K, p.tiles_n, p.nk, W);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+        const int grid = p.ntiles < dev.num_cu ? p.ntiles : dev.num_cu;
+        switch (nbands) {
+        case 5: e = launch_bands<5>(p, g.trans_a, grid, W, stream); break;
+        case 3: e = launch_bands<3>(p, g.trans_a, grid, W, stream); break;
+        default: e = launch_bands<2>(p, g.trans_a, grid, W, stream); break;
+        }
     }
+    const hipError_t ef = hipFreeAsync(W, stream);
+    return e != hipSuccess ? e : ef;
 }
 
 hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, hipStream_t stream)
