@@ -23,7 +23,7 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-ffp-contract=off",            # every fused multiply-add is written out explicitly
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1,0 +1,123 @@
+// Tiling, scheduling and data-movement helpers shared by the GEMM kernels
+// (gfx950 only).
+#pragma once
+
+#include "emu_device.h"
+#include "emu_launch.h"
+
+namespace emu {
+
+constexpr int BK = 32;             // k extent of one pipeline step
+constexpr int TILE = 128;          // output tile is TILE x TILE
+constexpr int LDS_ROW = BK + 8;    // bf16 elements per LDS row: 80 bytes, conflict-free 16-byte reads
+constexpr int LDSF_ROW = BK + 4;   // fp32 elements per LDS row (native kernel): 144 bytes
+
+// One GEMM call as the kernels see it (row-major; op(A) M x K, op(B) K x N).
+struct Params {
+    const float* A;
+    const float* B;
+    float* C;
+    int64_t lda, ldb, ldc;
+    int64_t M, N, K;
+    float alpha, beta;
+    int tiles_n;   // output tiles along N
+    int ntiles;    // output tiles in total
+    int nk;        // k-steps per tile
+    int vec_a;     // op(A) rows may be read with 16-byte loads
+    int vec_b;     // op(B) columns may be read with 16-byte loads (native kernel)
+};
+
+// Bijection on [0, G): hardware workgroup id -> position in the tile list.
+// Workgroup b runs on XCD b % 8; the workgroups of one XCD take a contiguous
+// range of positions, so tiles that share rows of A run on the same XCD and
+// share its L2.
+__device__ __forceinline__ int xcd_position(int b, int G)
+{
+    const int q = G >> 3, r = G & 7;
+    const int x = b & 7, s = b >> 3;
+    return x * q + (x < r ? x : r) + s;
+}
+
+// Position in the workgroup's static tile list plus k-step.  next()
+// saturates at the last (tile, k-step), so prefetches past the end re-read
+// valid data instead of running off the operands.  Tiles are ordered with n
+// fastest.
+struct Cursor {
+    int tile, kt, tn;
+    int64_t m0;
+    __device__ __forceinline__ void set(const Params& p, int t)
+    {
+        tile = t;
+        kt = 0;
+        const int tm = t / p.tiles_n;
+        tn = t - tm * p.tiles_n;
+        m0 = (int64_t)tm * TILE;
+    }
+    __device__ __forceinline__ void next(const Params& p, int G)
+    {
+        if (kt + 1 < p.nk)
+            ++kt;
+        else if (tile + G < p.ntiles)
+            set(p, tile + G);
+    }
+    __device__ __forceinline__ int64_t n0() const { return (int64_t)tn * TILE; }
+    __device__ __forceinline__ int64_t k0() const { return (int64_t)kt * BK; }
+};
+
+// Store one 32x32 MFMA result tile: lane l, register r holds row
+// 8*(r/4) + 4*(l/32) + r%4 and column l%32.  C = alpha t + beta C, C not
+// read when beta == 0.
+__device__ __forceinline__ void store_c_tile(const Params& p, const float (&t)[16], int64_t row0,
+                                             int64_t col0)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t col = col0 + (lane & 31);
+    if (col >= p.N) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < p.M) {
+            float* c = p.C + row * p.ldc + col;
+            float out = p.alpha * t[r];
+            if (p.beta != 0.0f) out = __builtin_fmaf(p.beta, *c, out);
+            *c = out;
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt
+    // (11:8) left at their maxima, i.e. not waited on.
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p)
+{
+    return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Direct global->LDS copy of 16 bytes per lane: lane l reads gbase + voff
+// and its bytes land at LDS offset lds_base + 16 l (gbase and lds_base
+// wave-uniform).  Inline assembly keeps the compiler from guarding later LDS
+// reads with waits for this load: the caller waits (wait_vmcnt) before the
+// barrier that publishes the data.
+__device__ __forceinline__ void copy16_to_lds(uint32_t lds_base, const void* gbase, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(uniform_ptr(gbase))
+                 : "memory");
+}
+
+}  // namespace emu
