@@ -34,11 +34,18 @@
 namespace emu {
 namespace {
 
-constexpr int NT = 512;            // threads per workgroup
-constexpr int WAVES_N = 4;         // waves along n (2 along m)
-constexpr int TM = 2;              // 32x32 tiles per wave along m
-constexpr int TN = 1;              // along n
 constexpr int PS = TILE * LDS_ROW; // elements per plane of an LDS tile
+
+// Workgroup shape: NT threads; waves arranged (NT/64/WN) x WN, each owning
+// TM x TN MFMA tiles of 32x32.
+template <int NT_, int WN_, int TM_, int TN_>
+struct Shape {
+    static constexpr int NT = NT_, WN = WN_, TM = TM_, TN = TN_;
+    static constexpr int WM = NT / 64 / WN;
+    static_assert(WM * TM * 32 == TILE && WN * TN * 32 == TILE, "waves must cover the tile");
+};
+using Shape8 = Shape<512, 4, 2, 1>;   // 8 waves (2 per SIMD), 64x32 each
+using Shape4 = Shape<256, 2, 2, 2>;   // 4 waves (1 per SIMD), 64x64 each
 
 __host__ __device__ constexpr int64_t chunk_elems(int np) { return (int64_t)np * PS; }
 
@@ -108,17 +115,20 @@ __global__ void presplit_kernel(const float* __restrict__ X, int64_t ld, int kc,
 //   3. wait for this step's direct loads; barrier.
 // The epilogue follows the tile's last step and clears the accumulators.
 // ---------------------------------------------------------------------------
-template <int NB, bool FUSED_A>
-__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Params p, const uint16_t* __restrict__ Wb,
-                                                          const uint16_t* __restrict__ Wa)
+template <class SH, int NB, bool FUSED_A>
+__global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const uint16_t* __restrict__ Wb,
+                                                              const uint16_t* __restrict__ Wa)
 {
+    constexpr int NT = SH::NT, WAVES_N = SH::WN, TM = SH::TM, TN = SH::TN;
+    constexpr int SROWS = TILE * 8 / NT;   // A rows split per thread (NT/8 rows apart)
     constexpr int NP = NB >= 3 ? 3 : 2;  // planes used: hi, mid' (, lo')
     constexpr int CHUNK_BYTES = (int)chunk_elems(NP) * 2;
     constexpr int COPY_ROUNDS = (CHUNK_BYTES + NT * 16 - 1) / (NT * 16);
     constexpr int STAGE_FLOATS = TILE * BK;
-    constexpr int STAGE_ROUNDS = STAGE_FLOATS * 4 / (NT * 16);   // 2
+    constexpr int STAGE_ROUNDS = STAGE_FLOATS * 4 / (NT * 16);
     constexpr int MFMA_PER_KS = TM * TN * (NB == 5 ? 9 : NB == 3 ? 6 : 3);
-    static_assert(STAGE_ROUNDS * NT * 16 == STAGE_FLOATS * 4, "staging copy rounds");
+    static_assert(STAGE_ROUNDS * NT * 16 == STAGE_FLOATS * 4 && STAGE_ROUNDS == SROWS,
+                  "each thread splits the rows it copied");
     __shared__ __attribute__((aligned(16))) uint16_t smA[2][chunk_elems(NP)];
     __shared__ __attribute__((aligned(16))) uint16_t smB[2][chunk_elems(NP)];
     __shared__ __attribute__((aligned(16))) float stage[FUSED_A ? 2 : 1][FUSED_A ? STAGE_FLOATS : 4];
@@ -135,16 +145,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Params p, const uint16
     const int frag_row = lane & 31;
     const int frag_k = (lane >> 5) * 8;
 
-    // Split/staging geometry: thread t owns rows t/8 and t/8 + 64, k t%8*4.
+    // Split/staging geometry: thread t owns rows t/8 + (NT/8) q, k t%8*4.
     const int srow = t >> 3;
     const int skc = (t & 7) * 4;
     // Direct-load byte offsets of the FP32 A tile (interior tiles).
     uint32_t a_off[STAGE_ROUNDS];
 #pragma unroll
     for (int r = 0; r < STAGE_ROUNDS; ++r)
-        a_off[r] = (uint32_t)(((int64_t)(srow + 64 * r) * p.lda + skc) * 4);
+        a_off[r] = (uint32_t)(((int64_t)(srow + (NT / 8) * r) * p.lda + skc) * 4);
 
-    auto copy_chunk = [&](const uint16_t* W, int64_t chunk, uint16_t* dst_tile) {
+    auto copy_chunk = [&](const uint16_t* W, int64_t chunk, uint16_t* dst_tile) __attribute__((always_inline)) {
         const char* src = reinterpret_cast<const char*>(W + chunk * chunk_elems(NP));
         const uint32_t dst = lds_offset(dst_tile);
 #pragma unroll
@@ -155,7 +165,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Params p, const uint16
     };
     // FP32 A tile of cursor c into staging buffer sb; rows past M and k past
     // K are redirected to valid addresses (their values are masked later).
-    auto copy_a32 = [&](const Cursor& c, int sb) {
+    auto copy_a32 = [&](const Cursor& c, int sb) __attribute__((always_inline)) {
         const float* base = p.A + c.m0 * p.lda + c.k0();
         const uint32_t dst = lds_offset(stage[sb]);
         const bool interior = c.m0 + TILE <= p.M && c.k0() + BK <= p.K;
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Params p, const uint16
         for (int r = 0; r < STAGE_ROUNDS; ++r) {
             uint32_t off = a_off[r];
             if (!interior) {
-                const int64_t row = srow + 64 * r;
+                const int64_t row = srow + (NT / 8) * r;
                 const int64_t rr = (c.m0 + row < p.M) ? row : (p.M - 1 - c.m0);
                 const int64_t kk = (c.k0() + skc < p.K) ? skc : 0;
                 off = (uint32_t)((rr * p.lda + kk) * 4);
@@ -174,7 +184,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Params p, const uint16
     // Step s (plane buffers pb = s%2): chunks of step s+1 into buffers pb^1,
     // FP32 A of step s+2 into staging buffer pb (its previous contents, step
     // s's A, were split during step s-1).
-    auto issue_loads = [&](const Cursor& cb, const Cursor& ca, int pb) {
+    auto issue_loads = [&](const Cursor& cb, const Cursor& ca, int pb) __attribute__((always_inline)) {
         copy_chunk(Wb, (int64_t)cb.tn * p.nk + cb.kt, smB[pb ^ 1]);
         if (FUSED_A)
             copy_a32(ca, pb);
@@ -184,11 +194,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Params p, const uint16
 
     // Split the FP32 tile in staging buffer sb (step described by c) into the
     // planes of plane buffer pb.
-    auto split_stage = [&](const Cursor& c, int sb, int pb) {
+    auto split_stage = [&](const Cursor& c, int sb, int pb) __attribute__((always_inline)) {
         const bool interior = c.m0 + TILE <= p.M && c.k0() + BK <= p.K;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int row = srow + 64 * q;
+        for (int q = 0; q < SROWS; ++q) {
+            const int row = srow + (NT / 8) * q;
             f32x4_t v = *reinterpret_cast<const f32x4_t*>(&stage[sb][row * BK + skc]);
             if (!interior) {
                 const bool rok = c.m0 + row < p.M;
@@ -220,7 +230,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Params p, const uint16
             for (int b = 0; b < NB; ++b) acc[i][j][b] = f32x16_t{};
 
     // MFMAs of k-half ks on plane buffer pb.
-    auto mfma_half = [&](int pb, int ks) {
+    auto mfma_half = [&](int pb, int ks) __attribute__((always_inline)) {
         const uint16_t* As = smA[pb];
         const uint16_t* Bs = smB[pb];
         bf16x8_t bfr[NP][TN];
@@ -248,8 +258,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Params p, const uint16
                     for (int i = 0; i < TM; ++i)
 #pragma unroll
                         for (int j = 0; j < TN; ++j)
+                            // B operand first: lane l then holds row m = l%32 of
+                            // its 32x32 block of C and four consecutive columns
+                            // per register group, for 16-byte stores.
                             acc[i][j][u + v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                af[i], bfr[v][j], acc[i][j][u + v], 0, 0, 0);
+                                bfr[v][j], af[i], acc[i][j][u + v], 0, 0, 0);
                 }
             }
         }
@@ -257,7 +270,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Params p, const uint16
 
     // One step's compute: the MFMAs of both k-halves, with (FUSED_A) the
     // split of the next step's A tile spread evenly between them.
-    auto compute = [&](int pb, const Cursor& cnext) {
+    auto compute = [&](int pb, const Cursor& cnext) __attribute__((always_inline)) {
         mfma_half(pb, 0);
         mfma_half(pb, 1);
         if (FUSED_A) {
@@ -270,26 +283,67 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Params p, const uint16
         }
     };
 
-    auto epilogue = [&](const Cursor& c) {
+    // Epilogue of the tile at cursor c: recombine the bands smallest first,
+    // C = alpha t + beta C, clear the accumulators.  Lane l holds, for each
+    // 32x32 block and register group g, row l%32 and columns 8g + 4(l/32)
+    // .. +3: one 16-byte buffer store per group, rows outside C given an
+    // out-of-range offset, so exactly EPI_STORES stores are issued whatever
+    // the tile's position (the step's vmcnt wait counts on it).  Tiles that
+    // cross column N, or C without 16-byte rows, store element by element.
+    constexpr int EPI_STORES = TM * TN * 4;
+    auto epilogue = [&](const Cursor& c) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(p.C + c.m0 * p.ldc + c.n0()), (short)0, 0x7FFFFFFF, 0x00020000);
+        const int64_t rows_left = p.M - c.m0, cols_left = p.N - c.n0();
+        const bool vec_c = p.vec_b != 0 && cols_left >= TILE;   // vec_b carries C's alignment
+        const int ldc4 = (int)p.ldc * 4;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                float tt[16];
+                const int row = (wm * TM + i) * 32 + (lane & 31);
+                const bool row_ok = row < rows_left;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float s = acc[i][j][NB - 1][r];
+                for (int g = 0; g < 4; ++g) {
+                    const int col = (wn * TN + j) * 32 + 8 * g + 4 * (lane >> 5);
+                    f32x4_t out;
 #pragma unroll
-                    for (int b = NB - 2; b >= 0; --b) s = __builtin_fmaf(s, 0.00390625f, acc[i][j][b][r]);
-                    tt[r] = s;
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * g + e;
+                        float s = acc[i][j][NB - 1][r];
+#pragma unroll
+                        for (int b = NB - 2; b >= 0; --b) s = __builtin_fmaf(s, 0.00390625f, acc[i][j][b][r]);
+                        out[e] = p.alpha * s;
+                    }
+                    if (vec_c) {
+                        const int off = row_ok ? row * ldc4 + col * 4 : (int)0x80000000;
+                        if (p.beta != 0.0f) {
+                            const f32x4_t old = __builtin_bit_cast(
+                                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(p.beta, old[e], out[e]);
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, out), rsrc,
+                                                               off, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (row_ok && col + e < cols_left) {
+                                float* cp = p.C + (c.m0 + row) * p.ldc + c.n0() + col + e;
+                                float o = out[e];
+                                if (p.beta != 0.0f) o = __builtin_fmaf(p.beta, *cp, o);
+                                *cp = o;
+                            }
+                        }
+                    }
                 }
-                store_c_tile(p, tt, c.m0 + (wm * TM + i) * 32, c.n0() + (wn * TN + j) * 32);
 #pragma unroll
                 for (int b = 0; b < NB; ++b) acc[i][j][b] = f32x16_t{};
             }
+        return vec_c;
     };
 
-    Cursor cc, cb, ca;   // compute step s, plane loads step s+1, FP32 A step s+2
+    Cursor cc, cb, ca;   // tile being computed, plane loads step s+1, FP32 A step s+2
     cc.set(p, slot);
     cb = cc;
     ca = cc;
@@ -310,21 +364,37 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Params p, const uint16
     ca.next(p, G);
     __syncthreads();
 
-    int kt = 0, pb = 0;
-    for (int s = 0; s < total; ++s) {
+    // One pipeline step.  EPI: the tile finished by the previous step gets its
+    // epilogue here, after this step's direct loads are issued, so the
+    // step's wait (vmcnt(EPI_STORES)) covers the loads and leaves the stores
+    // draining behind the next MFMAs.
+    int pb = 0;
+    auto step = [&]<bool EPI>(const Cursor& ce) __attribute__((always_inline)) {
         issue_loads(cb, ca, pb);
-        compute(pb, cb);
-        wait_vmcnt<0>();
-        __syncthreads();
-        if (kt == p.nk - 1) {
-            epilogue(cc);
-            if (cc.tile + G < p.ntiles) cc.set(p, cc.tile + G);
+        bool vec_stores = false;
+        if (EPI) {
+            vec_stores = epilogue(ce);
+            __builtin_amdgcn_sched_barrier(0);  // keep the next MFMAs' operand loads out of it
         }
+        compute(pb, cb);
+        if (vec_stores)
+            wait_vmcnt<EPI_STORES>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
         cb.next(p, G);
         ca.next(p, G);
-        kt = (kt + 1 == p.nk) ? 0 : kt + 1;
         pb ^= 1;
+    };
+
+    for (int kt = 0; kt < p.nk; ++kt) step.template operator()<false>(cc);
+    for (int tl = 1; tl < my_tiles; ++tl) {
+        const Cursor ce = cc;
+        cc.set(p, cc.tile + G);
+        step.template operator()<true>(ce);
+        for (int kt = 1; kt < p.nk; ++kt) step.template operator()<false>(cc);
     }
+    epilogue(cc);
 }
 
 int grid_for(int64_t work)
@@ -335,14 +405,17 @@ int grid_for(int64_t work)
     return (int)blocks;
 }
 
+using ShapeMain = Shape8;
+
 template <int NB>
 hipError_t launch_main(const Params& p, bool fused, int grid, const uint16_t* Wb,
                        const uint16_t* Wa, hipStream_t s)
 {
+    constexpr int NT = ShapeMain::NT;
     if (fused)
-        hipLaunchKernelGGL((gemm_bf16_kernel<NB, true>), dim3(grid), dim3(NT), 0, s, p, Wb, Wa);
+        hipLaunchKernelGGL((gemm_bf16_kernel<ShapeMain, NB, true>), dim3(grid), dim3(NT), 0, s, p, Wb, Wa);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<NB, false>), dim3(grid), dim3(NT), 0, s, p, Wb, Wa);
+        hipLaunchKernelGGL((gemm_bf16_kernel<ShapeMain, NB, false>), dim3(grid), dim3(NT), 0, s, p, Wb, Wa);
     return hipGetLastError();
 }
 
@@ -393,7 +466,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev
     const bool fused = !g.trans_a && ((uintptr_t)g.A & 15u) == 0 && (g.lda & 3) == 0 &&
                        (g.K & 3) == 0 && (int64_t)TILE * g.lda * 4 < ((int64_t)1 << 32);
     p.vec_a = fused ? 1 : 0;
-    p.vec_b = 0;
+    // (emulated kernel) C rows allow 16-byte stores at 16-byte aligned columns
+    p.vec_b = (((uintptr_t)g.C & 15u) == 0 && (g.ldc & 3) == 0 &&
+               (int64_t)TILE * g.ldc * 4 < ((int64_t)1 << 31)) ? 1 : 0;
 
     const int np = nbands >= 3 ? 3 : 2;
     const size_t bytes_b = (size_t)(tiles_n * nk * chunk_elems(np)) * sizeof(uint16_t);
