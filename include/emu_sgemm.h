@@ -23,7 +23,17 @@
  *       C stored M x N, ldc >= max(1, N)
  *     A column-major caller computes C^T = B^T A^T by swapping operands.
  *   - Every array pointer is device memory owned by the caller.  The library
- *     keeps no reference to it after the call returns and allocates nothing.
+ *     keeps no reference to it after the call returns.
+ *   - Memory: emu_sgemm in the BF16X* modes takes one stream-ordered
+ *     workspace for the BF16 planes of op(B), pre-split once per call (plus
+ *     those of op(A) when A cannot be split inside the GEMM: transA == T,
+ *     A not 16-byte aligned, or lda or K not a multiple of 4).  It is
+ *     allocated with hipMallocAsync from the device's default memory pool on
+ *     `stream` and released with hipFreeAsync on the same stream before the
+ *     call returns, so it lives exactly as long as the call's kernels.  Size
+ *     for B: planes * 2 bytes * ceil(N/128)*128 * ceil(K/32)*40 (3 planes,
+ *     2 in BF16X3; every 32 k-values of a row padded to 40), likewise with M
+ *     for A.  NATIVE_F32 and emu_split_bf16x3 allocate nothing.
  *   - stream is a hipStream_t (NULL = the null stream).  Work is enqueued on
  *     it asynchronously; errors during execution surface at the caller's
  *     next synchronisation of that stream.
@@ -61,7 +71,7 @@ typedef enum {
     EMU_STATUS_INVALID_VALUE = 1,  /* bad dimension, leading dimension, pointer or enum */
     EMU_STATUS_NOT_SUPPORTED = 2,  /* no gfx950 device current, or device query failed */
     EMU_STATUS_LAUNCH_FAILED = 3,  /* the kernel launch itself reported an error */
-    EMU_STATUS_ALLOC_FAILED = 4,   /* reserved: no entry point allocates */
+    EMU_STATUS_ALLOC_FAILED = 4,   /* the stream-ordered workspace could not be allocated */
     EMU_STATUS_INTERNAL = 5
 } emu_status_t;
 
@@ -91,8 +101,9 @@ typedef enum {
  * Errors: EMU_STATUS_INVALID_VALUE for M, N or K < 0, a leading dimension
  * below its bound, a NULL A or B with M*N*K > 0, a NULL C with M*N > 0, or a
  * transA/transB/mode outside its enum.  EMU_STATUS_NOT_SUPPORTED if the
- * current device is not gfx950.  EMU_STATUS_LAUNCH_FAILED if the launch
- * reports an error.
+ * current device is not gfx950.  EMU_STATUS_ALLOC_FAILED if the BF16X*
+ * workspace allocation fails (nothing was launched).  EMU_STATUS_LAUNCH_FAILED
+ * if a launch reports an error.
  */
 emu_status_t emu_sgemm(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
                        float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
