@@ -66,7 +66,7 @@ KERNEL_SOURCES = ("emulated_fp32_matrix_amd/csrc/emu_gemm_bf16.hip",
 # WRITE_SIZE) scaled by the same counters' reading for a 1 GiB device copy.
 # Keyed by the SHA-256 of KERNEL_SOURCES: a changed kernel reports null.
 TRAFFIC_BY_SOURCE = {
-    "3d7f098fc8db7faae942ffcc08339cc4866696a22a1ca1b37575313ffed3022d": 1894365701,
+    "562b0d82009d1f7b5a8acfc2ada07922f62772905a681c004790115c1e7a0436": 1939617040,
 }
 
 
@@ -210,8 +210,8 @@ def main():
             f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s")
 
     # Dominant kernel: every GEMM of the stack runs the same main kernel
-    # instantiation (A row-major and fused-split in both the forward NN and
-    # the input-gradient NT GEMM; B pre-split by a small kernel), so its
+    # instantiation (A row-major and split inside it in both the forward NN
+    # and the input-gradient NT GEMM; B pre-split by a small kernel), so its
     # average launch time is the per-GEMM event time averaged over the 8
     # GEMMs.  The event pair around each call also covers the B pre-split
     # (about 1 us), which the rocprofv3 summary lists separately.
@@ -225,7 +225,7 @@ def main():
         traffic = TRAFFIC_BY_SOURCE.get(kernel_source_hash())
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel": ("gemm_bf16_kernel<Shape<512,4,2,1>,%d,true>" % {9: 5, 6: 3, 3: 2}[P])
+                "kernel": ("gemm_bf16_pp_kernel<%d>" % {9: 5, 6: 3, 3: 2}[P])
                 if P > 1 else "gemm_f32_kernel",
                 "avg_launch_us": round(avg_us, 2),
                 "algorithmic_flop_per_launch": round(P * float(flops.sum()) / n_launch)}

@@ -21,12 +21,16 @@
 //     16-byte addressable, it is pre-split like B instead.
 //   * Persistent launch: one 512-thread workgroup per CU walks a static,
 //     XCD-aware list of 128x128 output tiles; the k-steps of consecutive
-//     tiles form one software pipeline with one barrier per step.
+//     tiles form one software pipeline.
 //   * 8 waves (two per SIMD) each own a 64x32 block of C as two
 //     v_mfma_f32_32x32x16_bf16 tiles with one FP32 accumulator per band
-//     (5 x 2 x 16 = 160 registers in the nine-product mode).  The split work
-//     of a step is interleaved with the step's MFMAs, so that the matrix
-//     unit keeps running while the vector ALU splits.
+//     (5 x 2 x 16 = 160 registers in the nine-product mode).
+//   * k-contiguous A (the forward and input-gradient GEMMs): the waves form
+//     two groups that take turns (gemm_bf16_pp_kernel): while one group's
+//     waves issue MFMAs, the other group's waves, one per SIMD beside them,
+//     load, split and store.  Otherwise (A transposed or not 16-byte
+//     addressable) A is pre-split like B and gemm_bf16_kernel runs, one
+//     barrier per step, the split work interleaved with the MFMAs.
 //   * Epilogue: bands are recombined smallest first (t = S_{n-1},
 //     t = S_j + 2^-8 t), then C = alpha t + beta C.
 #include "emu_tile.h"
@@ -397,6 +401,284 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
     epilogue(cc);
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong form of the GEMM kernel for a k-contiguous FP32 op(A) (split in
+// the kernel).  The 8 waves form two groups of four, one wave of each group
+// per SIMD; group g owns rows 64g..64g+63 of the 128x128 tile, each of its
+// waves a 64x32 block (two 32x32 MFMA tiles).  Each group alternates two
+// kinds of phase, each closed by a workgroup barrier:
+//   U(s): reads the group's FP32 A rows of step s+1 from staging, then
+//         (while those reads are in flight) the epilogue of the tile that
+//         ended at step s-1 and the direct loads of the A rows of step s+2
+//         and (group 1 only) of the B chunk of step s+1, then the split of
+//         the step s+1 rows into the other plane buffer;
+//   M(s): the MFMAs of step s.
+// Group 1 starts one phase late, so U of one group runs beside M of the
+// other: on every SIMD one wave keeps the matrix unit busy while the other
+// does the vector, LDS and memory work.  The split's LDS writes are only
+// waited for at the end of the next M phase, and each thread splits exactly
+// the A elements it loaded itself, so its own load-counter wait publishes
+// them to itself.
+// LDS: two plane buffers for A (each group touches only its own rows), two
+// B chunk buffers (B(s+1) is loaded while both groups may still read B(s)),
+// two FP32 staging buffers (step s+2 overwrites step s, split in U(s-1)).
+// ---------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const uint16_t* __restrict__ Wb)
+{
+    constexpr int NP = NB >= 3 ? 3 : 2;
+    constexpr int CHUNK_BYTES = (int)chunk_elems(NP) * 2;
+    constexpr int GT = 256;                                // threads per group
+    constexpr int GROWS = TILE / 2;                        // A rows per group
+    constexpr int B_ROUNDS = (CHUNK_BYTES + GT * 16 - 1) / (GT * 16);
+    constexpr int A_ROUNDS = GROWS * BK * 4 / (GT * 16);   // 16-byte loads per thread
+    constexpr int TM = 2;
+    static_assert(A_ROUNDS == 2 && GROWS == 2 * 32, "thread t splits rows t/8 and t/8 + 32 of its group");
+    __shared__ __attribute__((aligned(16))) uint16_t smA[2][chunk_elems(NP)];
+    __shared__ __attribute__((aligned(16))) uint16_t smB[2][chunk_elems(NP)];
+    __shared__ __attribute__((aligned(16))) float stage[2][TILE * BK];
+
+    const int G = gridDim.x;
+    const int slot = xcd_position(blockIdx.x, G);
+    const int my_tiles = (p.ntiles - slot + G - 1) / G;
+    const int total = my_tiles * p.nk;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
+    const int grp = wave >> 2;
+    const int gw = wave & 3;          // wave within the group = its 32-column block
+    const int gt = t & (GT - 1);
+    const int frag_row = lane & 31;
+    const int frag_k = (lane >> 5) * 8;
+
+    // Thread gt of group g loads and splits rows 64g + gt/8 + 32r (r = 0, 1),
+    // k = 4(gt%8) .. +3 of each step's FP32 A tile.
+    const int srow0 = GROWS * grp + (gt >> 3);
+    const int skc = (gt & 7) * 4;
+    uint32_t a_off[A_ROUNDS];
+#pragma unroll
+    for (int r = 0; r < A_ROUNDS; ++r)
+        a_off[r] = (uint32_t)(((int64_t)(srow0 + 32 * r) * p.lda + skc) * 4);
+
+    auto copy_a32 = [&](const Cursor& c, int sb) __attribute__((always_inline)) {
+        const float* base = p.A + c.m0 * p.lda + c.k0();
+        // staging is [128][32] floats: this wave's 64 lanes fill 1 KB at
+        // row 64g + 8 gw + 32 r
+        const uint32_t dst = lds_offset(stage[sb]) + 8192 * grp + 1024 * gw;
+        const bool interior = c.m0 + TILE <= p.M && c.k0() + BK <= p.K;
+#pragma unroll
+        for (int r = 0; r < A_ROUNDS; ++r) {
+            uint32_t off = a_off[r];
+            if (!interior) {
+                const int64_t row = srow0 + 32 * r;
+                const int64_t rr = (c.m0 + row < p.M) ? row : (p.M - 1 - c.m0);
+                const int64_t kk = (c.k0() + skc < p.K) ? skc : 0;
+                off = (uint32_t)((rr * p.lda + kk) * 4);
+            }
+            copy16_to_lds(dst + 4096 * r, base, off);
+        }
+    };
+    auto copy_b = [&](const Cursor& c, int bb) __attribute__((always_inline)) {
+        const char* src = reinterpret_cast<const char*>(Wb + ((int64_t)c.tn * p.nk + c.kt) * chunk_elems(NP));
+        const uint32_t dst = lds_offset(smB[bb]);
+#pragma unroll
+        for (int r = 0; r < B_ROUNDS; ++r) {
+            const int byte0 = (r * GT + gw * 64) * 16;   // this wave's 1 KB piece
+            if (byte0 < CHUNK_BYTES) copy16_to_lds(dst + byte0, src + byte0, (uint32_t)lane * 16);
+        }
+    };
+    // The split of the group's rows of one step, in two parts: load_rows
+    // reads the thread's FP32 values from staging buffer sb (elements
+    // outside op(A) selected to zero); split_rows splits them into plane
+    // buffer ab.  split_rows is pure VALU plus the final LDS writes, so it
+    // interleaves with the MFMAs.
+    auto load_rows = [&](const Cursor& c, int sb, f32x4_t (&v)[A_ROUNDS]) __attribute__((always_inline)) {
+        const int64_t rows_left = p.M - c.m0;
+        const int64_t k_left = p.K - c.k0();
+#pragma unroll
+        for (int q = 0; q < A_ROUNDS; ++q) {
+            const int row = srow0 + 32 * q;
+            v[q] = *reinterpret_cast<const f32x4_t*>(&stage[sb][row * BK + skc]);
+            const bool rok = row < rows_left;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[q][e] = (rok && skc + e < k_left) ? v[q][e] : 0.0f;
+        }
+    };
+    auto split_rows = [&](const f32x4_t (&v)[A_ROUNDS], int ab) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < A_ROUNDS; ++q) {
+            const int row = srow0 + 32 * q;
+            uint32_t h0, m0, l0, h1, m1, l1;
+            if (NP == 3) {
+                split_pair<true>(v[q][0], v[q][1], h0, m0, l0);
+                split_pair<true>(v[q][2], v[q][3], h1, m1, l1);
+            } else {
+                split_pair_hm(v[q][0], v[q][1], h0, m0);
+                split_pair_hm(v[q][2], v[q][3], h1, m1);
+            }
+            uint16_t* dst = smA[ab] + row * LDS_ROW + skc;
+            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{h0, h1};
+            *reinterpret_cast<u32x2_t*>(dst + PS) = u32x2_t{m0, m1};
+            if (NP == 3) *reinterpret_cast<u32x2_t*>(dst + 2 * PS) = u32x2_t{l0, l1};
+        }
+    };
+
+    f32x16_t acc[TM][NB];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[i][b] = f32x16_t{};
+
+    // MFMAs of k-half ks on buffers bb, smallest band first.
+    auto mfma_half = [&](int bb, int ks) __attribute__((always_inline)) {
+        const uint16_t* Bs = smB[bb];
+        const uint16_t* As = smA[bb];
+        bf16x8_t bfr[NP];
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl)
+            bfr[pl] = *reinterpret_cast<const bf16x8_t*>(Bs + pl * PS + (gw * 32 + frag_row) * LDS_ROW +
+                                                         ks * 16 + frag_k);
+#pragma unroll
+        for (int u = NP - 1; u >= 0; --u) {
+            bf16x8_t af[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8_t*>(
+                    As + u * PS + (grp * GROWS + i * 32 + frag_row) * LDS_ROW + ks * 16 + frag_k);
+#pragma unroll
+            for (int v = NP - 1; v >= 0; --v) {
+                if (u + v < NB) {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+                        // B operand first: lane l then holds row l%32 of the
+                        // 32x32 block and four consecutive columns per
+                        // register group, for 16-byte stores.
+                        acc[i][u + v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[v], af[i],
+                                                                                acc[i][u + v], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Epilogue of this wave's 64x32 block of the tile at cursor c: bands
+    // recombined smallest first, C = alpha t + beta C, accumulators cleared.
+    // Lane l holds, per 32x32 block and register group q, row l%32 and
+    // columns 8q + 4(l/32) .. +3: one 16-byte buffer store each, rows outside
+    // C given an out-of-range offset.  Tiles that cross column N, or C
+    // without 16-byte rows, store element by element.
+    auto epilogue = [&](const Cursor& c) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(p.C + c.m0 * p.ldc + c.n0()), (short)0, 0x7FFFFFFF, 0x00020000);
+        const int64_t rows_left = p.M - c.m0, cols_left = p.N - c.n0();
+        const bool vec_c = p.vec_b != 0 && cols_left >= TILE;   // vec_b carries C's alignment
+        const int ldc4 = (int)p.ldc * 4;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = grp * GROWS + i * 32 + (lane & 31);
+            const bool row_ok = row < rows_left;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = gw * 32 + 8 * q + 4 * (lane >> 5);
+                f32x4_t out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q + e;
+                    float sum = acc[i][NB - 1][r];
+#pragma unroll
+                    for (int b = NB - 2; b >= 0; --b) sum = __builtin_fmaf(sum, 0.00390625f, acc[i][b][r]);
+                    out[e] = p.alpha * sum;
+                }
+                if (vec_c) {
+                    const int off = row_ok ? row * ldc4 + col * 4 : (int)0x80000000;
+                    if (p.beta != 0.0f) {
+                        const f32x4_t old = __builtin_bit_cast(
+                            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(p.beta, old[e], out[e]);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, out), rsrc, off, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (row_ok && col + e < cols_left) {
+                            float* cp = p.C + (c.m0 + row) * p.ldc + c.n0() + col + e;
+                            float o = out[e];
+                            if (p.beta != 0.0f) o = __builtin_fmaf(p.beta, *cp, o);
+                            *cp = o;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[i][b] = f32x16_t{};
+        }
+    };
+
+    // Cursors: cm = step of the next M phase, ce = the step before it (its
+    // tile gets the epilogue when that step was the tile's last), cs = step
+    // split next, ca / cb = steps of the next A / B loads.
+    Cursor cm, ce, cs, ca, cb;
+    cm.set(p, slot);
+    ce = cm;
+    cs = cm;
+    ca = cm;
+    cb = cm;
+    // Prologue: B chunk of step 0; FP32 A rows of steps 0 and 1; split of
+    // step 0 into plane buffer 0.
+    if (grp == 1) copy_b(cb, 0);
+    cb.next(p, G);
+    copy_a32(ca, 0);
+    ca.next(p, G);
+    copy_a32(ca, 1);
+    ca.next(p, G);
+    wait_vmcnt<0>();
+    {
+        f32x4_t v0[A_ROUNDS];
+        load_rows(cs, 0, v0);
+        split_rows(v0, 0);
+    }
+    cs.next(p, G);
+    __syncthreads();
+    if (grp == 1) __builtin_amdgcn_s_barrier();   // group 1 runs one phase behind group 0
+
+    for (int s = 0; s < total; ++s) {
+        const int b = s & 1;
+        // ---- U(s).  The A rows of step s+1 were loaded in U(s-1) (or the
+        // prologue) into staging b^1.
+        wait_vmcnt<0>();
+        f32x4_t sv[A_ROUNDS];
+        load_rows(cs, b ^ 1, sv);
+        if (s > 0 && ce.kt == p.nk - 1) epilogue(ce);
+        if (grp == 1) copy_b(cb, b ^ 1);
+        cb.next(p, G);
+        copy_a32(ca, b);   // staging b held step s, split in U(s-1)
+        ca.next(p, G);
+        split_rows(sv, b ^ 1);   // plane buffer b^1 was last read by M(s-1)
+        cs.next(p, G);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();   // the split's writes drain during M(s)
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- M(s) on plane buffer b (split in U(s-1)) and B chunk b.
+        mfma_half(b, 0);
+        mfma_half(b, 1);
+        ce = cm;
+        cm.next(p, G);
+        // Before the next barrier: this thread's split writes of U(s) are
+        // complete (the group reads them in M(s+1)); group 1's B chunk of
+        // step s+1 has landed (group 0 reads it in M(s+1)), its A load of
+        // U(s) (the last A_ROUNDS issued) may still be in flight.
+        wait_lgkmcnt0();
+        if (grp == 1) wait_vmcnt<A_ROUNDS>();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    epilogue(ce);
+    wait_vmcnt<0>();   // no direct load may still be writing LDS when the workgroup ends
+    if (grp == 0) __builtin_amdgcn_s_barrier();   // matches group 1's extra barrier
+}
+
 int grid_for(int64_t work)
 {
     int64_t blocks = (work + 255) / 256;
@@ -413,7 +695,7 @@ hipError_t launch_main(const Params& p, bool fused, int grid, const uint16_t* Wb
 {
     constexpr int NT = ShapeMain::NT;
     if (fused)
-        hipLaunchKernelGGL((gemm_bf16_kernel<ShapeMain, NB, true>), dim3(grid), dim3(NT), 0, s, p, Wb, Wa);
+        hipLaunchKernelGGL((gemm_bf16_pp_kernel<NB>), dim3(grid), dim3(512), 0, s, p, Wb);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<ShapeMain, NB, false>), dim3(grid), dim3(NT), 0, s, p, Wb, Wa);
     return hipGetLastError();

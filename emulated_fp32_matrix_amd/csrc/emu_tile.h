@@ -94,6 +94,13 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
 }
 
+// Wait until all of this wave's LDS operations have completed (vmcnt and
+// expcnt left at their maxima).
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
 __device__ __forceinline__ uint32_t lds_offset(const void* p)
 {
     return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
