@@ -756,7 +756,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev
     const size_t bytes_b = (size_t)(tiles_n * nk * chunk_elems(np)) * sizeof(uint16_t);
     const size_t bytes_a = fused ? 0 : (size_t)(tiles_m * nk * chunk_elems(np)) * sizeof(uint16_t);
     uint16_t* ws = nullptr;
-    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), bytes_b + bytes_a, stream);
+    hipError_t e = dev.pool != nullptr
+                       ? hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), bytes_b + bytes_a, dev.pool, stream)
+                       : hipMallocAsync(reinterpret_cast<void**>(&ws), bytes_b + bytes_a, stream);
     if (e != hipSuccess) return hipErrorOutOfMemory;
     uint16_t* Wb = ws;
     uint16_t* Wa = fused ? nullptr : ws + bytes_b / sizeof(uint16_t);

@@ -21,8 +21,13 @@ struct GemmArgs {
 };
 
 struct DeviceInfo {
-    int num_cu;  // compute units of the current device
+    int num_cu;          // compute units of the current device
+    hipMemPool_t pool;   // library-owned pool for call workspaces (null: the device's default pool)
 };
+
+// Bytes of freed workspace the library's pool keeps mapped for reuse; larger
+// workspaces go back to the device at the stream's next synchronisation.
+constexpr uint64_t kPoolKeepBytes = 256ull << 20;
 
 // nbands: 5 (BF16X9), 3 (BF16X6) or 2 (BF16X3).
 hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev,

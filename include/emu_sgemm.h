@@ -28,9 +28,13 @@
  *     workspace for the BF16 planes of op(B), pre-split once per call (plus
  *     those of op(A) when A cannot be split inside the GEMM: transA == T,
  *     A not 16-byte aligned, or lda or K not a multiple of 4).  It is
- *     allocated with hipMallocAsync from the device's default memory pool on
- *     `stream` and released with hipFreeAsync on the same stream before the
- *     call returns, so it lives exactly as long as the call's kernels.  Size
+ *     allocated on `stream` from a memory pool the library creates once per
+ *     device (hipMallocFromPoolAsync; the device's default pool if creating
+ *     one fails) and released with hipFreeAsync on the same stream before
+ *     the call returns, so it lives exactly as long as the call's kernels.
+ *     The pool keeps up to 256 MiB of freed workspace mapped for reuse
+ *     until the process ends; larger workspaces are returned to the device
+ *     at the stream's next synchronisation.  Size
  *     for B: planes * 2 bytes * ceil(N/128)*128 * ceil(K/32)*40 (3 planes,
  *     2 in BF16X3; every 32 k-values of a row padded to 40), likewise with M
  *     for A.  NATIVE_F32 and emu_split_bf16x3 allocate nothing.
