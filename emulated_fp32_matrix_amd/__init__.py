@@ -32,8 +32,8 @@ STATUS_NOT_SUPPORTED = 2
 STATUS_LAUNCH_FAILED = 3
 
 # C functions declared in include/emu_sgemm.h
-EXPORTS = ("emu_sgemm", "emu_split_bf16x3", "emu_sgemm_select", "emu_status_string",
-           "emu_abi_version")
+EXPORTS = ("emu_sgemm", "emu_sgemm_bias", "emu_split_bf16x3", "emu_sgemm_select",
+           "emu_status_string", "emu_abi_version")
 
 
 class EmuError(RuntimeError):
@@ -61,6 +61,9 @@ _vp = ctypes.c_void_p
 _lib.emu_sgemm.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, _vp, _i64,
                            _vp, _i64, ctypes.c_float, _vp, _i64, ctypes.c_int, _vp]
 _lib.emu_sgemm.restype = ctypes.c_int
+_lib.emu_sgemm_bias.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, _vp,
+                                _i64, _vp, _i64, ctypes.c_float, _vp, _i64, _vp, ctypes.c_int, _vp]
+_lib.emu_sgemm_bias.restype = ctypes.c_int
 _lib.emu_split_bf16x3.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp]
 _lib.emu_split_bf16x3.restype = ctypes.c_int
 _lib.emu_sgemm_select.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64,
@@ -93,6 +96,14 @@ def emu_sgemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, mode
     return int(_lib.emu_sgemm(int(transA), int(transB), int(M), int(N), int(K), float(alpha),
                               A or None, int(lda), B or None, int(ldb), float(beta), C or None,
                               int(ldc), _mode(mode), stream or None))
+
+
+def emu_sgemm_bias(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, mode,
+                   stream) -> int:
+    """Raw call; returns the status code (pointers and stream are ints)."""
+    return int(_lib.emu_sgemm_bias(int(transA), int(transB), int(M), int(N), int(K), float(alpha),
+                                   A or None, int(lda), B or None, int(ldb), float(beta), C or None,
+                                   int(ldc), bias or None, _mode(mode), stream or None))
 
 
 def emu_split_bf16x3(x, n, hi, mid, lo, stream) -> int:
@@ -138,8 +149,9 @@ def _ld(x):
 
 
 def sgemm(a, b, mode="BF16X9", trans_a=False, trans_b=False, alpha=1.0, beta=0.0, c=None,
-          stream=None):
-    """C = alpha * op(a) @ op(b) + beta * c through ``emu_sgemm``.
+          stream=None, bias=None):
+    """C = alpha * op(a) @ op(b) + beta * c (+ bias[j] on every row) through
+    ``emu_sgemm`` (``emu_sgemm_bias`` when ``bias`` is given).
 
     ``a``/``b`` are the stored (row-major) matrices; ``trans_*`` select op().
     Returns ``c`` (allocated when None).  Asynchronous on ``stream``
@@ -160,11 +172,21 @@ def sgemm(a, b, mode="BF16X9", trans_a=False, trans_b=False, alpha=1.0, beta=0.0
         _check_matrix(c, "c")
         if tuple(c.shape) != (M, N):
             raise ValueError(f"c must be {M}x{N}")
-    st = emu_sgemm(OP_T if trans_a else OP_N, OP_T if trans_b else OP_N, M, N, K, alpha,
-                   a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), beta, c.data_ptr(), _ld(c),
-                   mode, _stream_handle(stream))
+    if bias is None:
+        st = emu_sgemm(OP_T if trans_a else OP_N, OP_T if trans_b else OP_N, M, N, K, alpha,
+                       a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), beta, c.data_ptr(), _ld(c),
+                       mode, _stream_handle(stream))
+        if st != STATUS_SUCCESS:
+            raise EmuError(st, "emu_sgemm")
+        return c
+    if (not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or not bias.is_cuda
+            or bias.dim() != 1 or bias.shape[0] != N or (N > 1 and bias.stride(0) != 1)):
+        raise TypeError(f"bias must be a contiguous float32 CUDA vector of length {N}")
+    st = emu_sgemm_bias(OP_T if trans_a else OP_N, OP_T if trans_b else OP_N, M, N, K, alpha,
+                        a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), beta, c.data_ptr(), _ld(c),
+                        bias.data_ptr(), mode, _stream_handle(stream))
     if st != STATUS_SUCCESS:
-        raise EmuError(st, "emu_sgemm")
+        raise EmuError(st, "emu_sgemm_bias")
     return c
 
 

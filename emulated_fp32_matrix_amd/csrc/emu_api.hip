@@ -124,35 +124,12 @@ emu_status_t from_hip(hipError_t e)
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-const char* emu_status_string(emu_status_t status)
-{
-    switch (status) {
-    case EMU_STATUS_SUCCESS: return "EMU_STATUS_SUCCESS";
-    case EMU_STATUS_INVALID_VALUE: return "EMU_STATUS_INVALID_VALUE";
-    case EMU_STATUS_NOT_SUPPORTED: return "EMU_STATUS_NOT_SUPPORTED";
-    case EMU_STATUS_LAUNCH_FAILED: return "EMU_STATUS_LAUNCH_FAILED";
-    case EMU_STATUS_ALLOC_FAILED: return "EMU_STATUS_ALLOC_FAILED";
-    case EMU_STATUS_INTERNAL: return "EMU_STATUS_INTERNAL";
-    default: return "EMU_STATUS_UNKNOWN";
-    }
-}
-
-int emu_abi_version(void) { return 100; }
-
-emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
-                              emu_mode_t* chosen)
-{
-    if (!valid_op(transA) || !valid_op(transB) || M < 0 || N < 0 || K < 0 || chosen == nullptr)
-        return EMU_STATUS_INVALID_VALUE;
-    *chosen = select_mode(M, N, K);
-    return EMU_STATUS_SUCCESS;
-}
-
-emu_status_t emu_sgemm(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
-                       float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
-                       float beta, float* C, int64_t ldc, emu_mode_t mode, void* stream)
+emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
+                        float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                        float beta, float* C, int64_t ldc, const float* bias, emu_mode_t mode,
+                        void* stream)
 {
     // ---- validation: no HIP call before this block has passed ----
     if (!valid_op(transA) || !valid_op(transB)) return EMU_STATUS_INVALID_VALUE;
@@ -171,7 +148,7 @@ emu_status_t emu_sgemm(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, i
     if (!current_device(dev)) return EMU_STATUS_NOT_SUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    if (K == 0 || alpha == 0.0f) return from_hip(emu::launch_scale_c(M, N, beta, C, ldc, s));
+    if (K == 0 || alpha == 0.0f) return from_hip(emu::launch_scale_c(M, N, beta, C, ldc, bias, s));
 
     if (mode == EMU_MODE_AUTO) mode = select_mode(M, N, K);
     emu::GemmArgs g;
@@ -188,6 +165,7 @@ emu_status_t emu_sgemm(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, i
     g.ldb = ldb;
     g.C = C;
     g.ldc = ldc;
+    g.bias = bias;
     switch (mode) {
     case EMU_MODE_NATIVE_F32: return from_hip(emu::launch_gemm_native_f32(g, dev, s));
     case EMU_MODE_BF16X9: return from_hip(emu::launch_gemm_bf16(g, 5, dev, s));
@@ -195,6 +173,51 @@ emu_status_t emu_sgemm(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, i
     case EMU_MODE_BF16X3: return from_hip(emu::launch_gemm_bf16(g, 2, dev, s));
     default: return EMU_STATUS_INTERNAL;
     }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* emu_status_string(emu_status_t status)
+{
+    switch (status) {
+    case EMU_STATUS_SUCCESS: return "EMU_STATUS_SUCCESS";
+    case EMU_STATUS_INVALID_VALUE: return "EMU_STATUS_INVALID_VALUE";
+    case EMU_STATUS_NOT_SUPPORTED: return "EMU_STATUS_NOT_SUPPORTED";
+    case EMU_STATUS_LAUNCH_FAILED: return "EMU_STATUS_LAUNCH_FAILED";
+    case EMU_STATUS_ALLOC_FAILED: return "EMU_STATUS_ALLOC_FAILED";
+    case EMU_STATUS_INTERNAL: return "EMU_STATUS_INTERNAL";
+    default: return "EMU_STATUS_UNKNOWN";
+    }
+}
+
+int emu_abi_version(void) { return 101; }
+
+emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
+                              emu_mode_t* chosen)
+{
+    if (!valid_op(transA) || !valid_op(transB) || M < 0 || N < 0 || K < 0 || chosen == nullptr)
+        return EMU_STATUS_INVALID_VALUE;
+    *chosen = select_mode(M, N, K);
+    return EMU_STATUS_SUCCESS;
+}
+
+emu_status_t emu_sgemm(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
+                       float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                       float beta, float* C, int64_t ldc, emu_mode_t mode, void* stream)
+{
+    return sgemm_impl(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, nullptr, mode,
+                      stream);
+}
+
+emu_status_t emu_sgemm_bias(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
+                            float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                            float beta, float* C, int64_t ldc, const float* bias, emu_mode_t mode,
+                            void* stream)
+{
+    return sgemm_impl(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, mode,
+                      stream);
 }
 
 emu_status_t emu_split_bf16x3(const float* x, int64_t n, uint16_t* hi, uint16_t* mid,

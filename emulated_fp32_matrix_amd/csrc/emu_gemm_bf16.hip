@@ -140,7 +140,6 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
     const int G = gridDim.x;
     const int slot = xcd_position(blockIdx.x, G);
     const int my_tiles = (p.ntiles - slot + G - 1) / G;
-    const int total = my_tiles * p.nk;
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -327,6 +326,11 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 #pragma unroll
                             for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(p.beta, old[e], out[e]);
                         }
+                        if (p.bias != nullptr) {
+                            const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.bias + c.n0() + col);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) out[e] = out[e] + bv[e];
+                        }
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, out), rsrc,
                                                                off, 0, 0);
                     } else {
@@ -336,6 +340,7 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
                                 float* cp = p.C + (c.m0 + row) * p.ldc + c.n0() + col + e;
                                 float o = out[e];
                                 if (p.beta != 0.0f) o = __builtin_fmaf(p.beta, *cp, o);
+                                if (p.bias != nullptr) o = o + p.bias[c.n0() + col + e];
                                 *cp = o;
                             }
                         }
@@ -597,6 +602,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
 #pragma unroll
                         for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(p.beta, old[e], out[e]);
                     }
+                    if (p.bias != nullptr) {
+                        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.bias + c.n0() + col);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) out[e] = out[e] + bv[e];
+                    }
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, out), rsrc, off, 0, 0);
                 } else {
 #pragma unroll
@@ -605,6 +615,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
                             float* cp = p.C + (c.m0 + row) * p.ldc + c.n0() + col + e;
                             float o = out[e];
                             if (p.beta != 0.0f) o = __builtin_fmaf(p.beta, *cp, o);
+                            if (p.bias != nullptr) o = o + p.bias[c.n0() + col + e];
                             *cp = o;
                         }
                     }
@@ -740,6 +751,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev
     p.K = g.K;
     p.alpha = g.alpha;
     p.beta = g.beta;
+    p.bias = g.bias;
     p.tiles_n = (int)tiles_n;
     p.ntiles = (int)(tiles_m * tiles_n);
     p.nk = (int)nk;
@@ -748,8 +760,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev
     const bool fused = !g.trans_a && ((uintptr_t)g.A & 15u) == 0 && (g.lda & 3) == 0 &&
                        (g.K & 3) == 0 && (int64_t)TILE * g.lda * 4 < ((int64_t)1 << 32);
     p.vec_a = fused ? 1 : 0;
-    // (emulated kernel) C rows allow 16-byte stores at 16-byte aligned columns
+    // (emulated kernels) C rows allow 16-byte stores at 16-byte aligned
+    // columns, and the bias (if any) 16-byte loads there
     p.vec_b = (((uintptr_t)g.C & 15u) == 0 && (g.ldc & 3) == 0 &&
+               (g.bias == nullptr || ((uintptr_t)g.bias & 15u) == 0) &&
                (int64_t)TILE * g.ldc * 4 < ((int64_t)1 << 31)) ? 1 : 0;
 
     const int np = nbands >= 3 ? 3 : 2;

@@ -202,14 +202,16 @@ __global__ __launch_bounds__(GEO::NT, 2) void gemm_f32_kernel(Params p)
 }
 
 __global__ void scale_c_kernel(int64_t M, int64_t N, float beta, float* __restrict__ C,
-                               int64_t ldc)
+                               int64_t ldc, const float* __restrict__ bias)
 {
     const int64_t total = M * N;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
          e += (int64_t)gridDim.x * blockDim.x) {
         const int64_t i = e / N, j = e - i * N;
         float* c = C + i * ldc + j;
-        *c = (beta == 0.0f) ? 0.0f : beta * *c;
+        float out = (beta == 0.0f) ? 0.0f : beta * *c;
+        if (bias != nullptr) out = out + bias[j];
+        *c = out;
     }
 }
 
@@ -227,6 +229,7 @@ Params make_params(const GemmArgs& g, int bm, int bn)
     p.K = g.K;
     p.alpha = g.alpha;
     p.beta = g.beta;
+    p.bias = g.bias;
     const int64_t tiles_m = (g.M + bm - 1) / bm;
     const int64_t tiles_n = (g.N + bn - 1) / bn;
     p.tiles_n = (int)tiles_n;
@@ -273,14 +276,14 @@ hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, hipS
 }
 
 hipError_t launch_scale_c(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
-                          hipStream_t stream)
+                          const float* bias, hipStream_t stream)
 {
     const int64_t total = M * N;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(scale_c_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, M, N, beta, C,
-                       ldc);
+                       ldc, bias);
     return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ struct GemmArgs {
     int64_t ldb;
     float* C;
     int64_t ldc;
+    const float* bias;   // length N or null
 };
 
 struct DeviceInfo {
@@ -33,9 +34,9 @@ constexpr uint64_t kPoolKeepBytes = 256ull << 20;
 hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev,
                             hipStream_t stream);
 hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, hipStream_t stream);
-// C = beta * C over M x N (zeroes C without reading it when beta == 0).
+// C = beta * C + bias over M x N (C not read when beta == 0; bias may be null).
 hipError_t launch_scale_c(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
-                          hipStream_t stream);
+                          const float* bias, hipStream_t stream);
 hipError_t launch_split(const float* x, int64_t n, uint16_t* hi, uint16_t* mid, uint16_t* lo,
                         hipStream_t stream);
 

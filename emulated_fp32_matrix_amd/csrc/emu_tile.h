@@ -20,6 +20,7 @@ struct Params {
     int64_t lda, ldb, ldc;
     int64_t M, N, K;
     float alpha, beta;
+    const float* bias;   // length N, added to every row of C after alpha/beta; null: none
     int tiles_n;   // output tiles along N
     int ntiles;    // output tiles in total
     int nk;        // k-steps per tile
@@ -65,14 +66,15 @@ struct Cursor {
 };
 
 // Store one 32x32 MFMA result tile: lane l, register r holds row
-// 8*(r/4) + 4*(l/32) + r%4 and column l%32.  C = alpha t + beta C, C not
-// read when beta == 0.
+// 8*(r/4) + 4*(l/32) + r%4 and column l%32.  C = alpha t + beta C + bias,
+// C not read when beta == 0.
 __device__ __forceinline__ void store_c_tile(const Params& p, const float (&t)[16], int64_t row0,
                                              int64_t col0)
 {
     const int lane = threadIdx.x & 63;
     const int64_t col = col0 + (lane & 31);
     if (col >= p.N) return;
+    const float bias = p.bias != nullptr ? p.bias[col] : 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int64_t row = row0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -80,6 +82,7 @@ __device__ __forceinline__ void store_c_tile(const Params& p, const float (&t)[1
             float* c = p.C + row * p.ldc + col;
             float out = p.alpha * t[r];
             if (p.beta != 0.0f) out = __builtin_fmaf(p.beta, *c, out);
+            if (p.bias != nullptr) out = out + bias;
             *c = out;
         }
     }

@@ -114,6 +114,25 @@ emu_status_t emu_sgemm(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, i
                        float beta, float* C, int64_t ldc, emu_mode_t mode, void* stream);
 
 /*
+ * emu_sgemm with a bias fused into the epilogue, for the linear layer of
+ * "Unlocking Tensor Core Performance for Machine Learning Interatomic
+ * Potentials", section "TF32x3 on Ampere GPUs" (a float-in / float-out
+ * layer that behaves like a standard linear layer, y = x W^T + b):
+ *
+ *   C[i][j] = alpha * (op(A) . op(B))[i][j] + beta * C[i][j] + bias[j]
+ *
+ * in FP32, the bias added last, after alpha and beta.  bias: N floats of
+ * device memory, any alignment (16-byte aligned takes the vectorised path),
+ * owned by the caller; NULL means no bias (then identical to emu_sgemm).  With
+ * K == 0 or alpha == 0: C = beta * C + bias.  Everything else (modes,
+ * layout, workspace, errors, asynchrony) is as for emu_sgemm.
+ */
+emu_status_t emu_sgemm_bias(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
+                            float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                            float beta, float* C, int64_t ldc, const float* bias, emu_mode_t mode,
+                            void* stream);
+
+/*
  * The exact three-piece split on its own (Figure 1): for i < n,
  *   hi[i], mid[i], lo[i] = BF16 bit patterns of hi, mid', lo' of x[i]
  * with x[i] == hi + 2^-8 mid' + 2^-16 lo' exactly for every finite x[i].
@@ -142,7 +161,8 @@ emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64
  * codes give "EMU_STATUS_UNKNOWN".  Never NULL. */
 const char* emu_status_string(emu_status_t status);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor): 101 (1.1 added
+ * emu_sgemm_bias). */
 int emu_abi_version(void);
 
 #ifdef __cplusplus

@@ -106,8 +106,23 @@ def _shapes(a, b, trans_a, trans_b):
     return M, N, K
 
 
-def gemm_f64(a, b, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, c=None) -> np.ndarray:
-    """FP64-accumulated alpha*op(A)@op(B) + beta*C of FP32 inputs (float64 M x N)."""
+def _bias(bias, N):
+    if bias is None:
+        return None
+    bias = _f32(bias)
+    if bias.shape != (N,):
+        raise ValueError(f"bias must have shape ({N},)")
+    return bias
+
+
+def gemm_f64(a, b, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, c=None,
+             bias=None) -> np.ndarray:
+    """FP64-accumulated alpha*op(A)@op(B) + beta*C of FP32 inputs (float64 M x N).
+
+    ``bias`` (length N, FP32) is added to every row last, in FP64: the linear
+    layer y = x W^T + b of "Unlocking Tensor Core Performance for Machine
+    Learning Interatomic Potentials", section "TF32x3 on Ampere GPUs".
+    """
     a = _f32(a)
     b = _f32(b)
     M, N, K = _shapes(a, b, trans_a, trans_b)
@@ -118,17 +133,22 @@ def gemm_f64(a, b, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, c=None) ->
         cp, ldc = _ptr(c), N
     else:
         cp, ldc = None, max(N, 1)
+    bias = _bias(bias, N)
     _load().oracle_gemm_f64(int(trans_a), int(trans_b), M, N, K, float(alpha), _ptr(a),
                             a.shape[1], _ptr(b), b.shape[1], float(beta), cp, ldc, _ptr(out))
+    if bias is not None:
+        out += bias.astype(np.float64)[None, :]
     return out
 
 
 def emu_gemm(a, b, mode="BF16X9", trans_a=False, trans_b=False, alpha=1.0, beta=0.0, c=None,
-             acc_f64=False) -> np.ndarray:
+             acc_f64=False, bias=None) -> np.ndarray:
     """Scalar model of the emulated GEMM.
 
     ``mode`` is BF16X9, BF16X6 or BF16X3 (or an explicit band count 1..5).
     Returns float32 (FP32 band accumulation) or float64 (``acc_f64``).
+    ``bias`` (length N) is added to every row after alpha and beta, with one
+    more rounding in the output's precision.
     """
     nb = NBANDS[mode] if isinstance(mode, str) else int(mode)
     a = _f32(a)
@@ -146,8 +166,14 @@ def emu_gemm(a, b, mode="BF16X9", trans_a=False, trans_b=False, alpha=1.0, beta=
         cp, ldc = _ptr(c), N
     else:
         cp, ldc = None, max(N, 1)
+    bias = _bias(bias, N)
     _load().oracle_emu_gemm(int(trans_a), int(trans_b), M, N, K, nb, int(acc_f64), float(alpha),
                             _ptr(a), a.shape[1], _ptr(b), b.shape[1], float(beta), cp, ldc,
                             _ptr(out32) if out32 is not None else None,
                             _ptr(out64) if out64 is not None else None)
+    if bias is not None:
+        if acc_f64:
+            out64 += bias.astype(np.float64)[None, :]
+        else:
+            out32 = (out32 + bias[None, :]).astype(np.float32)   # one float32 rounding per entry
     return out64 if acc_f64 else out32

@@ -45,7 +45,7 @@ def test_status_strings_and_version():
     assert emu.emu_status_string(2) == "EMU_STATUS_NOT_SUPPORTED"
     assert emu.emu_status_string(3) == "EMU_STATUS_LAUNCH_FAILED"
     assert emu.emu_status_string(99) == "EMU_STATUS_UNKNOWN"
-    assert emu.emu_abi_version() == 100
+    assert emu.emu_abi_version() == 101
 
 
 FAKE = 0x1000  # never dereferenced: validation fails (or returns) before any HIP call
@@ -80,10 +80,23 @@ def test_invalid_arguments_rejected(args):
     assert emu.emu_sgemm(**call) == emu.STATUS_INVALID_VALUE
 
 
+@pytest.mark.parametrize("args", [
+    dict(transA=2), dict(mode=7), dict(M=-1), dict(K=-1), dict(lda=7), dict(ldb=5), dict(ldc=5),
+    dict(A=0), dict(B=0), dict(C=0),
+])
+def test_bias_entry_point_invalid_arguments_rejected(args):
+    call = dict(transA=0, transB=0, M=10, N=6, K=8, alpha=1.0, A=FAKE, lda=8, B=FAKE, ldb=6,
+                beta=0.0, C=FAKE, ldc=6, bias=FAKE, mode=1, stream=0)
+    call.update(args)
+    assert emu.emu_sgemm_bias(**call) == emu.STATUS_INVALID_VALUE
+
+
 def test_empty_shapes_return_before_touching_the_device():
     base = dict(transA=0, transB=0, alpha=1.0, A=0, B=0, beta=0.0, C=0, mode=1, stream=0)
     assert emu.emu_sgemm(M=0, N=5, K=4, lda=4, ldb=5, ldc=5, **base) == emu.STATUS_SUCCESS
     assert emu.emu_sgemm(M=5, N=0, K=4, lda=4, ldb=1, ldc=1, **base) == emu.STATUS_SUCCESS
+    assert emu.emu_sgemm_bias(M=0, N=5, K=4, lda=4, ldb=5, ldc=5, bias=0, **base) == \
+        emu.STATUS_SUCCESS
     assert emu.emu_split_bf16x3(0, 0, 0, 0, 0, 0) == emu.STATUS_SUCCESS
 
 

@@ -250,3 +250,45 @@ def test_emu_matches_fp64_on_config0():
     ref = oracle.gemm_f64(a, b)
     out = oracle.emu_gemm(a, b, "BF16X9")
     assert _err_f(out, ref) <= 2e-6
+
+
+# ---------------------------------------------------------------- bias (linear layer)
+
+def test_bias_identity_closed_form():
+    """B = I (K = N) makes the GEMM part exactly op(A) in every mode's band
+    model (X9, X6) and in FP64; the bias is then one FP32 addition per entry
+    (one FP64 addition for the reference), added to column j of every row.
+    M != N, so a bias indexed by row instead of column would fail."""
+    rng = np.random.default_rng(11)
+    M, N = 7, 5
+    a = rng.standard_normal((M, N)).astype(np.float32)
+    eye = np.eye(N, dtype=np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    expect32 = (a + bias[None, :]).astype(np.float32)
+    for mode in ("BF16X9", "BF16X6"):
+        out = oracle.emu_gemm(a, eye, mode, bias=bias)
+        assert out.dtype == np.float32 and np.array_equal(out, expect32), mode
+    ref = oracle.gemm_f64(a, eye, bias=bias)
+    assert np.array_equal(ref, a.astype(np.float64) + bias.astype(np.float64)[None, :])
+
+
+def test_bias_with_zero_k_and_beta():
+    """K = 0: the product is empty, so C = beta*C + bias exactly as written."""
+    rng = np.random.default_rng(12)
+    M, N = 4, 6
+    a = np.zeros((M, 0), np.float32)
+    b = np.zeros((0, N), np.float32)
+    c = rng.standard_normal((M, N)).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    ref = oracle.gemm_f64(a, b, beta=0.5, c=c, bias=bias)
+    assert np.array_equal(ref, 0.5 * c.astype(np.float64) + bias.astype(np.float64)[None, :])
+
+
+def test_bias_matches_numpy_float64():
+    rng = np.random.default_rng(13)
+    a = rng.standard_normal((9, 13)).astype(np.float32)
+    b = rng.standard_normal((13, 11)).astype(np.float32)
+    bias = rng.standard_normal(11).astype(np.float32)
+    ref = oracle.gemm_f64(a, b, bias=bias)
+    want = a.astype(np.float64) @ b.astype(np.float64) + bias.astype(np.float64)
+    assert np.max(np.abs(ref - want)) <= 1e-13 * np.max(np.abs(want))
