@@ -1,0 +1,113 @@
+"""EmuLinear: a float-in / float-out linear layer whose forward GEMM and
+input-gradient GEMM run through the emulated-FP32 library.
+
+"Unlocking Tensor Core Performance for Machine Learning Interatomic
+Potentials", section "TF32x3 on Ampere GPUs", describes such a layer: a
+drop-in replacement for a standard linear layer, FP32 tensors in and out,
+whose forward product and the gradient propagated to its input (from which
+an interatomic potential derives forces) both use the emulated arithmetic,
+while the weight gradient stays in ordinary precision.
+
+Here, with the weight stored like torch.nn.Linear ([out_features,
+in_features]):
+  forward   y  = x W^T + b   emu_sgemm_bias, op(B) = W^T (transB = T), bias
+                             added in the GEMM epilogue;
+  backward  dx = dy W        emu_sgemm (transB = N);
+            dW = dy^T x      torch FP32 matmul (TF32 off), db = sum of dy rows.
+
+The mode ("AUTO" = the performant policy, "BF16X9" = eager, "BF16X6",
+"BF16X3", "NATIVE_F32") applies to both library GEMMs.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import sgemm
+
+
+def _as_rows(t, width):
+    t2 = t.reshape(-1, width)
+    return t2 if t2.is_contiguous() else t2.contiguous()
+
+
+class _EmuLinearFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, weight, bias, mode):
+        if x.dtype != torch.float32 or weight.dtype != torch.float32:
+            raise TypeError("EmuLinear computes in float32")
+        out_f, in_f = weight.shape
+        x2 = _as_rows(x, in_f)
+        w = weight if weight.is_contiguous() else weight.contiguous()
+        y = sgemm(x2, w, mode=mode, trans_b=True, bias=bias)
+        ctx.save_for_backward(x2, w)
+        ctx.has_bias = bias is not None
+        ctx.mode = mode
+        ctx.x_shape = x.shape
+        return y.reshape(*x.shape[:-1], out_f)
+
+    @staticmethod
+    def backward(ctx, gy):
+        x2, w = ctx.saved_tensors
+        out_f, in_f = w.shape
+        gy2 = _as_rows(gy, out_f)
+        gx = gw = gb = None
+        if ctx.needs_input_grad[0]:
+            gx = sgemm(gy2, w, mode=ctx.mode).reshape(ctx.x_shape)
+        if ctx.needs_input_grad[1]:
+            prev = torch.backends.cuda.matmul.allow_tf32
+            torch.backends.cuda.matmul.allow_tf32 = False
+            try:
+                gw = gy2.t().matmul(x2)
+            finally:
+                torch.backends.cuda.matmul.allow_tf32 = prev
+        if ctx.has_bias and ctx.needs_input_grad[2]:
+            gb = gy2.sum(dim=0)
+        return gx, gw, gb, None
+
+
+class EmuLinear(torch.nn.Module):
+    """torch.nn.Linear with its forward and input-gradient GEMMs emulated.
+
+    Parameters and initialisation match torch.nn.Linear, so state dicts load
+    either way; :meth:`from_linear` wraps an existing layer's parameters.
+    """
+
+    def __init__(self, in_features, out_features, bias=True, mode="AUTO", device=None):
+        super().__init__()
+        self.in_features = in_features
+        self.out_features = out_features
+        self.mode = mode
+        self.weight = torch.nn.Parameter(torch.empty(out_features, in_features, device=device,
+                                                     dtype=torch.float32))
+        if bias:
+            self.bias = torch.nn.Parameter(torch.empty(out_features, device=device,
+                                                       dtype=torch.float32))
+        else:
+            self.register_parameter("bias", None)
+        self.reset_parameters()
+
+    def reset_parameters(self):
+        # the same scheme as torch.nn.Linear
+        torch.nn.init.kaiming_uniform_(self.weight, a=math.sqrt(5))
+        if self.bias is not None:
+            bound = 1.0 / math.sqrt(self.in_features) if self.in_features > 0 else 0.0
+            torch.nn.init.uniform_(self.bias, -bound, bound)
+
+    @classmethod
+    def from_linear(cls, linear, mode="AUTO"):
+        m = cls(linear.in_features, linear.out_features, bias=linear.bias is not None, mode=mode,
+                device=linear.weight.device)
+        with torch.no_grad():
+            m.weight.copy_(linear.weight)
+            if linear.bias is not None:
+                m.bias.copy_(linear.bias)
+        return m
+
+    def forward(self, x):
+        return _EmuLinearFunction.apply(x, self.weight, self.bias, self.mode)
+
+    def extra_repr(self):
+        return (f"in_features={self.in_features}, out_features={self.out_features}, "
+                f"bias={self.bias is not None}, mode={self.mode}")
