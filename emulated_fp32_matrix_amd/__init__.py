@@ -24,7 +24,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libemu_sgemm.so")
 
 OP_N, OP_T = 0, 1
-MODES = {"NATIVE_F32": 0, "BF16X9": 1, "BF16X6": 2, "BF16X3": 3, "AUTO": 4}
+MODES = {"NATIVE_F32": 0, "BF16X9": 1, "BF16X6": 2, "BF16X3": 3, "AUTO": 4, "BF16X1": 5}
 MODE_NAMES = {v: k for k, v in MODES.items()}
 STATUS_SUCCESS = 0
 STATUS_INVALID_VALUE = 1

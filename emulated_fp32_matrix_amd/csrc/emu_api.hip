@@ -133,7 +133,7 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
 {
     // ---- validation: no HIP call before this block has passed ----
     if (!valid_op(transA) || !valid_op(transB)) return EMU_STATUS_INVALID_VALUE;
-    if ((int)mode < (int)EMU_MODE_NATIVE_F32 || (int)mode > (int)EMU_MODE_AUTO)
+    if ((int)mode < (int)EMU_MODE_NATIVE_F32 || (int)mode > (int)EMU_MODE_BF16X1)
         return EMU_STATUS_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return EMU_STATUS_INVALID_VALUE;
     if (lda < (transA == EMU_OP_N ? max1(K) : max1(M))) return EMU_STATUS_INVALID_VALUE;
@@ -171,6 +171,7 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     case EMU_MODE_BF16X9: return from_hip(emu::launch_gemm_bf16(g, 5, dev, s));
     case EMU_MODE_BF16X6: return from_hip(emu::launch_gemm_bf16(g, 3, dev, s));
     case EMU_MODE_BF16X3: return from_hip(emu::launch_gemm_bf16(g, 2, dev, s));
+    case EMU_MODE_BF16X1: return from_hip(emu::launch_gemm_bf16(g, 1, dev, s));
     default: return EMU_STATUS_INTERNAL;
     }
 }
@@ -192,7 +193,7 @@ const char* emu_status_string(emu_status_t status)
     }
 }
 
-int emu_abi_version(void) { return 101; }
+int emu_abi_version(void) { return 102; }
 
 emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
                               emu_mode_t* chosen)

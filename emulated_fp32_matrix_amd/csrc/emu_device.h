@@ -72,4 +72,19 @@ __device__ __forceinline__ void split_pair_hm(float a0, float a1, uint32_t& hi, 
     mid = pack_bf16x2(m0, m1);
 }
 
+// The first NP pieces of a pair (a0 in the low half of each word):
+// w[0] = hi, w[1] = mid', w[2] = lo'.  NP = 1 is the one-piece (hi only)
+// rounding of the one-product mode.
+template <int NP>
+__device__ __forceinline__ void split_pieces(float a0, float a1, uint32_t (&w)[NP])
+{
+    static_assert(NP >= 1 && NP <= 3, "one to three pieces");
+    if constexpr (NP == 3)
+        split_pair<true>(a0, a1, w[0], w[1], w[2]);
+    else if constexpr (NP == 2)
+        split_pair_hm(a0, a1, w[0], w[1]);
+    else
+        w[0] = pack_bf16x2(clamp_sat(a0), clamp_sat(a1));
+}
+
 }  // namespace emu

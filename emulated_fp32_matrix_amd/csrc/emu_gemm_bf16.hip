@@ -84,22 +84,16 @@ __global__ void presplit_kernel(const float* __restrict__ X, int64_t ld, int kc,
             const int64_t k = k0 + e;
             v[e] = (r < rows && k < K) ? (kc ? X[r * ld + k] : X[k * ld + r]) : 0.0f;
         }
-        uint32_t h[4], m[4], l[4];
+        uint32_t w[4][NP];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (NP == 3)
-                split_pair<true>(v[2 * e], v[2 * e + 1], h[e], m[e], l[e]);
-            else
-                split_pair_hm(v[2 * e], v[2 * e + 1], h[e], m[e]);
-        }
+        for (int e = 0; e < 4; ++e) split_pieces<NP>(v[2 * e], v[2 * e + 1], w[e]);
         const int64_t tr = r / TILE, rr = r - tr * TILE;
         const int64_t kt = k0 / BK, kk = k0 - kt * BK;
         uint16_t* chunk = W + (tr * nk + kt) * chunk_elems(NP);
         const int64_t off = rr * LDS_ROW + kk;
-        *reinterpret_cast<u32x4_t*>(chunk + off) = u32x4_t{h[0], h[1], h[2], h[3]};
-        *reinterpret_cast<u32x4_t*>(chunk + PS + off) = u32x4_t{m[0], m[1], m[2], m[3]};
-        if (NP == 3)
-            *reinterpret_cast<u32x4_t*>(chunk + 2 * PS + off) = u32x4_t{l[0], l[1], l[2], l[3]};
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl)
+            *reinterpret_cast<u32x4_t*>(chunk + pl * PS + off) = u32x4_t{w[0][pl], w[1][pl], w[2][pl], w[3][pl]};
     }
 }
 
@@ -125,12 +119,12 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 {
     constexpr int NT = SH::NT, WAVES_N = SH::WN, TM = SH::TM, TN = SH::TN;
     constexpr int SROWS = TILE * 8 / NT;   // A rows split per thread (NT/8 rows apart)
-    constexpr int NP = NB >= 3 ? 3 : 2;  // planes used: hi, mid' (, lo')
+    constexpr int NP = NB >= 3 ? 3 : NB;  // planes used: hi (, mid' (, lo'))
     constexpr int CHUNK_BYTES = (int)chunk_elems(NP) * 2;
     constexpr int COPY_ROUNDS = (CHUNK_BYTES + NT * 16 - 1) / (NT * 16);
     constexpr int STAGE_FLOATS = TILE * BK;
     constexpr int STAGE_ROUNDS = STAGE_FLOATS * 4 / (NT * 16);
-    constexpr int MFMA_PER_KS = TM * TN * (NB == 5 ? 9 : NB == 3 ? 6 : 3);
+    constexpr int MFMA_PER_KS = TM * TN * (NB == 5 ? 9 : NB == 3 ? 6 : NB == 2 ? 3 : 1);
     static_assert(STAGE_ROUNDS * NT * 16 == STAGE_FLOATS * 4 && STAGE_ROUNDS == SROWS,
                   "each thread splits the rows it copied");
     __shared__ __attribute__((aligned(16))) uint16_t smA[2][chunk_elems(NP)];
@@ -209,18 +203,12 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
                 for (int e = 0; e < 4; ++e)
                     if (!(rok && c.k0() + skc + e < p.K)) v[e] = 0.0f;
             }
-            uint32_t h0, m0, l0, h1, m1, l1;
-            if (NP == 3) {
-                split_pair<true>(v[0], v[1], h0, m0, l0);
-                split_pair<true>(v[2], v[3], h1, m1, l1);
-            } else {
-                split_pair_hm(v[0], v[1], h0, m0);
-                split_pair_hm(v[2], v[3], h1, m1);
-            }
+            uint32_t w0[NP], w1[NP];
+            split_pieces<NP>(v[0], v[1], w0);
+            split_pieces<NP>(v[2], v[3], w1);
             uint16_t* dst = smA[pb] + row * LDS_ROW + skc;
-            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{h0, h1};
-            *reinterpret_cast<u32x2_t*>(dst + PS) = u32x2_t{m0, m1};
-            if (NP == 3) *reinterpret_cast<u32x2_t*>(dst + 2 * PS) = u32x2_t{l0, l1};
+#pragma unroll
+            for (int pl = 0; pl < NP; ++pl) *reinterpret_cast<u32x2_t*>(dst + pl * PS) = u32x2_t{w0[pl], w1[pl]};
         }
     };
 
@@ -431,7 +419,7 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 template <int NB>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const uint16_t* __restrict__ Wb)
 {
-    constexpr int NP = NB >= 3 ? 3 : 2;
+    constexpr int NP = NB >= 3 ? 3 : NB;
     constexpr int CHUNK_BYTES = (int)chunk_elems(NP) * 2;
     constexpr int GT = 256;                                // threads per group
     constexpr int GROWS = TILE / 2;                        // A rows per group
@@ -514,18 +502,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
 #pragma unroll
         for (int q = 0; q < A_ROUNDS; ++q) {
             const int row = srow0 + 32 * q;
-            uint32_t h0, m0, l0, h1, m1, l1;
-            if (NP == 3) {
-                split_pair<true>(v[q][0], v[q][1], h0, m0, l0);
-                split_pair<true>(v[q][2], v[q][3], h1, m1, l1);
-            } else {
-                split_pair_hm(v[q][0], v[q][1], h0, m0);
-                split_pair_hm(v[q][2], v[q][3], h1, m1);
-            }
+            uint32_t w0[NP], w1[NP];
+            split_pieces<NP>(v[q][0], v[q][1], w0);
+            split_pieces<NP>(v[q][2], v[q][3], w1);
             uint16_t* dst = smA[ab] + row * LDS_ROW + skc;
-            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{h0, h1};
-            *reinterpret_cast<u32x2_t*>(dst + PS) = u32x2_t{m0, m1};
-            if (NP == 3) *reinterpret_cast<u32x2_t*>(dst + 2 * PS) = u32x2_t{l0, l1};
+#pragma unroll
+            for (int pl = 0; pl < NP; ++pl) *reinterpret_cast<u32x2_t*>(dst + pl * PS) = u32x2_t{w0[pl], w1[pl]};
         }
     };
 
@@ -719,8 +701,11 @@ hipError_t launch_presplit(int np, const float* X, int64_t ld, bool kc, int64_t 
     if (np == 3)
         hipLaunchKernelGGL(presplit_kernel<3>, dim3(grid), dim3(256), 0, s, X, ld, kc ? 1 : 0, rows,
                            K, tiles_r, nk, W);
-    else
+    else if (np == 2)
         hipLaunchKernelGGL(presplit_kernel<2>, dim3(grid), dim3(256), 0, s, X, ld, kc ? 1 : 0, rows,
+                           K, tiles_r, nk, W);
+    else
+        hipLaunchKernelGGL(presplit_kernel<1>, dim3(grid), dim3(256), 0, s, X, ld, kc ? 1 : 0, rows,
                            K, tiles_r, nk, W);
     return hipGetLastError();
 }
@@ -730,7 +715,7 @@ hipError_t launch_presplit(int np, const float* X, int64_t ld, bool kc, int64_t 
 hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev,
                             hipStream_t stream)
 {
-    if (nbands != 5 && nbands != 3 && nbands != 2) return hipErrorInvalidValue;
+    if (nbands != 5 && nbands != 3 && nbands != 2 && nbands != 1) return hipErrorInvalidValue;
     const int64_t tiles_m = (g.M + TILE - 1) / TILE;
     const int64_t tiles_n = (g.N + TILE - 1) / TILE;
     const int64_t nk = (g.K + BK - 1) / BK;
@@ -766,7 +751,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev
                (g.bias == nullptr || ((uintptr_t)g.bias & 15u) == 0) &&
                (int64_t)TILE * g.ldc * 4 < ((int64_t)1 << 31)) ? 1 : 0;
 
-    const int np = nbands >= 3 ? 3 : 2;
+    const int np = nbands >= 3 ? 3 : nbands;
     const size_t bytes_b = (size_t)(tiles_n * nk * chunk_elems(np)) * sizeof(uint16_t);
     const size_t bytes_a = fused ? 0 : (size_t)(tiles_m * nk * chunk_elems(np)) * sizeof(uint16_t);
     uint16_t* ws = nullptr;
@@ -785,7 +770,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev
         switch (nbands) {
         case 5: e = launch_main<5>(p, fused, grid, Wb, Wa, stream); break;
         case 3: e = launch_main<3>(p, fused, grid, Wb, Wa, stream); break;
-        default: e = launch_main<2>(p, fused, grid, Wb, Wa, stream); break;
+        case 2: e = launch_main<2>(p, fused, grid, Wb, Wa, stream); break;
+        default: e = launch_main<1>(p, fused, grid, Wb, Wa, stream); break;
         }
     }
     const hipError_t ef = hipFreeAsync(ws, stream);

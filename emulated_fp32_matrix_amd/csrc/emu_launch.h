@@ -30,7 +30,7 @@ struct DeviceInfo {
 // workspaces go back to the device at the stream's next synchronisation.
 constexpr uint64_t kPoolKeepBytes = 256ull << 20;
 
-// nbands: 5 (BF16X9), 3 (BF16X6) or 2 (BF16X3).
+// nbands: 5 (BF16X9), 3 (BF16X6), 2 (BF16X3) or 1 (BF16X1).
 hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev,
                             hipStream_t stream);
 hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, hipStream_t stream);

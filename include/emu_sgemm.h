@@ -67,7 +67,12 @@ typedef enum {
     EMU_MODE_BF16X3 = 3,
     /* Per-shape choice between NATIVE_F32 and BF16X9, the "performant"
      * policy of section "BF16x9 on NVIDIA Blackwell GPUs". */
-    EMU_MODE_AUTO = 4
+    EMU_MODE_AUTO = 4,
+    /* One product hi*hi: band 0 only, operands rounded once to BF16, the
+     * analog of the single-pass TF32 mode that section "TF32x3 on Ampere
+     * GPUs" compares TF32x3 against.  Not FP32-accurate (about 2^-8
+     * relative per product); never chosen by AUTO.  (ABI 1.2) */
+    EMU_MODE_BF16X1 = 5
 } emu_mode_t;
 
 typedef enum {
@@ -82,12 +87,12 @@ typedef enum {
 /*
  * C = alpha * op(A) . op(B) + beta * C in FP32, computed in `mode`.
  *
- * BF16X9/X6/X3: each element of op(A) and op(B) is split exactly into
+ * BF16X9/X6/X3 (and BF16X1): each element of op(A) and op(B) is split exactly into
  * (hi, mid', lo') with hi = R(a), mid' = R(2^8 (a - hi)), lo' = 2^8 (2^8 (a -
  * hi) - mid'), R = round to nearest even, saturating at the largest finite
  * BF16 (Figure 1's "three scaled BF16 components").  Products with piece
- * indices u + v = j are accumulated in FP32 band j; the bands kept (5, 3 or
- * 2) are recombined smallest first, t = S_{n-1}, t = S_j + 2^-8 t, and then
+ * indices u + v = j are accumulated in FP32 band j; the bands kept (5, 3, 2
+ * or 1) are recombined smallest first, t = S_{n-1}, t = S_j + 2^-8 t, and then
  * C = alpha * t + beta * C.
  *
  * Semantics follow BLAS SGEMM:
@@ -161,8 +166,8 @@ emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64
  * codes give "EMU_STATUS_UNKNOWN".  Never NULL. */
 const char* emu_status_string(emu_status_t status);
 
-/* ABI version of this header (major * 100 + minor): 101 (1.1 added
- * emu_sgemm_bias). */
+/* ABI version of this header (major * 100 + minor): 102 (1.1 added
+ * emu_sgemm_bias, 1.2 EMU_MODE_BF16X1). */
 int emu_abi_version(void);
 
 #ifdef __cplusplus

@@ -28,7 +28,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-NBANDS = {"BF16X9": 5, "BF16X6": 3, "BF16X3": 2}
+NBANDS = {"BF16X9": 5, "BF16X6": 3, "BF16X3": 2, "BF16X1": 1}
 
 
 def _load():

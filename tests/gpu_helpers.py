@@ -23,7 +23,7 @@ import numpy as np
 import oracle
 
 FLT_MAX = float(np.finfo(np.float32).max)
-DELTA = {"NATIVE_F32": 0.0, "BF16X9": 0.0, "BF16X6": 2.0**-22, "BF16X3": 2.0**-14}
+DELTA = {"NATIVE_F32": 0.0, "BF16X9": 0.0, "BF16X6": 2.0**-22, "BF16X3": 2.0**-14, "BF16X1": 2.0**-7}
 MODES = ("NATIVE_F32", "BF16X9", "BF16X6", "BF16X3")
 
 

@@ -45,7 +45,7 @@ def test_status_strings_and_version():
     assert emu.emu_status_string(2) == "EMU_STATUS_NOT_SUPPORTED"
     assert emu.emu_status_string(3) == "EMU_STATUS_LAUNCH_FAILED"
     assert emu.emu_status_string(99) == "EMU_STATUS_UNKNOWN"
-    assert emu.emu_abi_version() == 101
+    assert emu.emu_abi_version() == 102
 
 
 FAKE = 0x1000  # never dereferenced: validation fails (or returns) before any HIP call
@@ -54,7 +54,7 @@ FAKE = 0x1000  # never dereferenced: validation fails (or returns) before any HI
 @pytest.mark.parametrize("args", [
     dict(transA=2),
     dict(transB=-1),
-    dict(mode=5),
+    dict(mode=6),
     dict(mode=-1),
     dict(M=-1),
     dict(N=-3),

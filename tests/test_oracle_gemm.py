@@ -32,7 +32,7 @@ import oracle
 import synth
 
 TRANS = list(itertools.product([False, True], [False, True]))
-DELTA = {"BF16X9": 0.0, "BF16X6": 2.0**-22, "BF16X3": 2.0**-14}
+DELTA = {"BF16X9": 0.0, "BF16X6": 2.0**-22, "BF16X3": 2.0**-14, "BF16X1": 2.0**-7}
 
 
 def _op(x, t):
@@ -150,7 +150,7 @@ def _componentwise_ok(out, a, b, K, mode, alpha=1.0, beta=0.0, c=None):
     return bool(np.all(diff <= bound)), float(np.max(diff / np.where(bound > 0, bound, 1.0)))
 
 
-@pytest.mark.parametrize("mode", ["BF16X9", "BF16X6", "BF16X3"])
+@pytest.mark.parametrize("mode", ["BF16X9", "BF16X6", "BF16X3", "BF16X1"])
 @pytest.mark.parametrize("ta,tb", TRANS)
 def test_emu_componentwise_bound(mode, ta, tb):
     rng = np.random.default_rng(5)
@@ -189,6 +189,8 @@ def test_emu_identity_closed_form(ta, tb):
             expect = (h + m * 2.0**-8).astype(np.float32)
             assert np.array_equal(expect.astype(np.float64), h + m * 2.0**-8)  # exact in FP32
             assert np.array_equal(out, expect)
+        elif mode == "BF16X1":
+            assert np.array_equal(out, h.astype(np.float32))   # A rounded once to BF16
         else:
             assert np.array_equal(out.view(np.uint32) & 0x7FFFFFFF, a.view(np.uint32) & 0x7FFFFFFF)
             assert np.array_equal(out, a)
@@ -233,7 +235,7 @@ def test_exact_band_error_ordering_and_accuracy_claim():
             out = oracle.emu_gemm(a, b, mode, acc_f64=True)
             d = (out - ref)[fin]
             errs[mode] = float(np.linalg.norm(d) / np.linalg.norm(ref[fin]))
-        assert errs["BF16X3"] > errs["BF16X6"] > errs["BF16X9"], (dist, errs)
+        assert errs["BF16X1"] > errs["BF16X3"] > errs["BF16X6"] > errs["BF16X9"], (dist, errs)
         # with FP32 band accumulation, X9 is at least as accurate as FP32 matmul
         x9 = oracle.emu_gemm(a, b, "BF16X9")
         f32 = (a @ b).astype(np.float32)
