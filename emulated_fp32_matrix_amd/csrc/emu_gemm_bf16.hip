@@ -401,21 +401,79 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 // waves a 64x32 block (two 32x32 MFMA tiles).  Each group alternates two
 // kinds of phase, each closed by a workgroup barrier:
 //   U(s): reads the group's FP32 A rows of step s+1 from staging, then
-//         (while those reads are in flight) the epilogue of the tile that
-//         ended at step s-1 and the direct loads of the A rows of step s+2
-//         and (group 1 only) of the B chunk of step s+1, then the split of
-//         the step s+1 rows into the other plane buffer;
-//   M(s): the MFMAs of step s.
+//         (while those reads are in flight) issues the direct loads of the
+//         B chunk of step s+1 (group 1 only) and of the A rows of step s+2,
+//         runs the epilogue of the tile that ended at step s-1 (its stores
+//         issued after the loads, so that waiting for the loads never waits
+//         for them), then splits the step s+1 rows into the other plane
+//         buffer;
+//   M(s): the MFMAs of step s, and the scalar bookkeeping (advancing the
+//         step cursors, precomputing addresses) for the next U phase.
 // Group 1 starts one phase late, so U of one group runs beside M of the
 // other: on every SIMD one wave keeps the matrix unit busy while the other
-// does the vector, LDS and memory work.  The split's LDS writes are only
-// waited for at the end of the next M phase, and each thread splits exactly
-// the A elements it loaded itself, so its own load-counter wait publishes
-// them to itself.
+// does the vector, LDS and memory work.  Since a wave issues one instruction
+// at a time, scalar work costs issue slots in a U phase but fills idle ones
+// between the MFMAs of an M phase, which is where it is placed.  An M
+// phase's fragment reads run one group of MFMAs ahead of their use, the
+// first group's before the barrier.  The split's LDS writes are only waited
+// for at the end of the next M phase, and each thread splits exactly the A
+// elements it loaded itself, so its own load-counter wait publishes them to
+// itself.
 // LDS: two plane buffers for A (each group touches only its own rows), two
 // B chunk buffers (B(s+1) is loaded while both groups may still read B(s)),
 // two FP32 staging buffers (step s+2 overwrites step s, split in U(s-1)).
 // ---------------------------------------------------------------------------
+
+// A position (tile, k-step) in a workgroup's static sequence, advanced without
+// divisions: the workgroup's tiles are t0, t0 + G, t0 + 2G, ... (n fastest),
+// so each advance adds G / tiles_n tile rows and G % tiles_n tile columns.
+// Past the last step it stays put (prefetches re-read valid data).
+struct Walk {
+    int kt;          // k-step
+    int tn;          // tile column
+    int left;        // tiles after this one
+    int64_t m0;      // first row
+    int64_t arow;    // m0 * lda (element offset of the tile's first A row)
+    int rows;        // rows of the tile inside op(A): min(M - m0, TILE)
+    int kvalid;      // k of this step inside op(A): min(K - 32 kt, 32)
+};
+
+// The tile a finished step belonged to (what the epilogue needs of a Walk).
+struct TilePos {
+    int64_t m0;
+    int tn, rows;
+};
+
+struct WalkConst {
+    int nk, tiles_n, gtn, tail_k;   // tail_k: valid k of the last step
+    int64_t gm, M, lda;             // gm: rows added per advance
+};
+
+__device__ __forceinline__ void walk_set_tile(Walk& w, const WalkConst& c)
+{
+    w.arow = w.m0 * c.lda;
+    const int64_t r = c.M - w.m0;
+    w.rows = r < TILE ? (int)r : TILE;
+}
+
+__device__ __forceinline__ void walk_next(Walk& w, const WalkConst& c)
+{
+    if (w.kt + 1 < c.nk) {
+        ++w.kt;
+    } else if (w.left > 0) {
+        --w.left;
+        w.kt = 0;
+        w.tn += c.gtn;
+        w.m0 += c.gm;
+        if (w.tn >= c.tiles_n) {
+            w.tn -= c.tiles_n;
+            w.m0 += TILE;
+        }
+        walk_set_tile(w, c);
+    }
+    w.kvalid = w.kt + 1 < c.nk ? BK : c.tail_k;
+}
+
 template <int NB>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const uint16_t* __restrict__ Wb)
 {
@@ -436,6 +494,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     const int my_tiles = (p.ntiles - slot + G - 1) / G;
     const int total = my_tiles * p.nk;
 
+    WalkConst wc;
+    wc.nk = p.nk;
+    wc.tiles_n = p.tiles_n;
+    wc.gtn = G % p.tiles_n;
+    wc.gm = (int64_t)(G / p.tiles_n) * TILE;
+    wc.tail_k = (int)(p.K - (int64_t)(p.nk - 1) * BK);
+    wc.M = p.M;
+    wc.lda = p.lda;
+
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
@@ -454,48 +521,54 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     for (int r = 0; r < A_ROUNDS; ++r)
         a_off[r] = (uint32_t)(((int64_t)(srow0 + 32 * r) * p.lda + skc) * 4);
 
-    auto copy_a32 = [&](const Cursor& c, int sb) __attribute__((always_inline)) {
-        const float* base = p.A + c.m0 * p.lda + c.k0();
-        // staging is [128][32] floats: this wave's 64 lanes fill 1 KB at
-        // row 64g + 8 gw + 32 r
+    // Round r (of A_ROUNDS) of the group's FP32 A rows of step w into
+    // staging buffer sb: staging is [128][32] floats, this wave's 64 lanes
+    // fill 1 KB at row 64g + 8 gw + 32 r.
+    auto copy_a32_round = [&](const Walk& w, int sb, int r) __attribute__((always_inline)) {
+        const float* base = p.A + w.arow + (int64_t)w.kt * BK;
         const uint32_t dst = lds_offset(stage[sb]) + 8192 * grp + 1024 * gw;
-        const bool interior = c.m0 + TILE <= p.M && c.k0() + BK <= p.K;
-#pragma unroll
-        for (int r = 0; r < A_ROUNDS; ++r) {
-            uint32_t off = a_off[r];
-            if (!interior) {
-                const int64_t row = srow0 + 32 * r;
-                const int64_t rr = (c.m0 + row < p.M) ? row : (p.M - 1 - c.m0);
-                const int64_t kk = (c.k0() + skc < p.K) ? skc : 0;
-                off = (uint32_t)((rr * p.lda + kk) * 4);
-            }
-            copy16_to_lds(dst + 4096 * r, base, off);
+        uint32_t off = a_off[r];
+        if (w.rows != TILE || w.kvalid != BK) {
+            // rows past M re-read the tile's last row, k past K column 0
+            // (both masked when split)
+            const int row = srow0 + 32 * r;
+            const int64_t rr = row < w.rows ? row : w.rows - 1;
+            const int kk = skc < w.kvalid ? skc : 0;
+            off = (uint32_t)((rr * p.lda + kk) * 4);
         }
+        copy16_to_lds(dst + 4096 * r, base, off);
     };
-    auto copy_b = [&](const Cursor& c, int bb) __attribute__((always_inline)) {
-        const char* src = reinterpret_cast<const char*>(Wb + ((int64_t)c.tn * p.nk + c.kt) * chunk_elems(NP));
+    auto copy_a32 = [&](const Walk& w, int sb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < A_ROUNDS; ++r) copy_a32_round(w, sb, r);
+    };
+    // Rounds [r0, r1) of the group's copy of the B chunk of step w into
+    // buffer bb: round r moves the 4 KB at 4096 r, this wave's 1 KB piece of
+    // it at 4096 r + 1024 gw (the last round may be partial).
+    auto copy_b_rounds = [&](const Walk& w, int bb, int r0, int r1) __attribute__((always_inline)) {
+        const char* src = reinterpret_cast<const char*>(Wb + ((int64_t)w.tn * p.nk + w.kt) * chunk_elems(NP));
         const uint32_t dst = lds_offset(smB[bb]);
 #pragma unroll
-        for (int r = 0; r < B_ROUNDS; ++r) {
-            const int byte0 = (r * GT + gw * 64) * 16;   // this wave's 1 KB piece
+        for (int r = r0; r < r1; ++r) {
+            const int byte0 = (r * GT + gw * 64) * 16;
             if (byte0 < CHUNK_BYTES) copy16_to_lds(dst + byte0, src + byte0, (uint32_t)lane * 16);
         }
     };
     // The split of the group's rows of one step, in two parts: load_rows
-    // reads the thread's FP32 values from staging buffer sb (elements
-    // outside op(A) selected to zero); split_rows splits them into plane
-    // buffer ab.  split_rows is pure VALU plus the final LDS writes, so it
-    // interleaves with the MFMAs.
-    auto load_rows = [&](const Cursor& c, int sb, f32x4_t (&v)[A_ROUNDS]) __attribute__((always_inline)) {
-        const int64_t rows_left = p.M - c.m0;
-        const int64_t k_left = p.K - c.k0();
+    // reads the thread's FP32 values from staging buffer sb (on edge tiles,
+    // elements outside op(A) selected to zero); split_rows splits them into
+    // plane buffer ab.
+    auto load_rows = [&](const Walk& w, int sb, f32x4_t (&v)[A_ROUNDS]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < A_ROUNDS; ++q) {
-            const int row = srow0 + 32 * q;
-            v[q] = *reinterpret_cast<const f32x4_t*>(&stage[sb][row * BK + skc]);
-            const bool rok = row < rows_left;
+        for (int q = 0; q < A_ROUNDS; ++q)
+            v[q] = *reinterpret_cast<const f32x4_t*>(&stage[sb][(srow0 + 32 * q) * BK + skc]);
+        if (w.rows != TILE || w.kvalid != BK) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[q][e] = (rok && skc + e < k_left) ? v[q][e] : 0.0f;
+            for (int q = 0; q < A_ROUNDS; ++q) {
+                const bool rok = srow0 + 32 * q < w.rows;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[q][e] = (rok && skc + e < w.kvalid) ? v[q][e] : 0.0f;
+            }
         }
     };
     auto split_rows = [&](const f32x4_t (&v)[A_ROUNDS], int ab) __attribute__((always_inline)) {
@@ -511,59 +584,64 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         }
     };
 
+    // Accumulators: cleared here and by each tile's epilogue.
     f32x16_t acc[TM][NB];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[i][b] = f32x16_t{};
 
-    // MFMAs of k-half ks on buffers bb, smallest band first.
-    auto mfma_half = [&](int bb, int ks) __attribute__((always_inline)) {
-        const uint16_t* Bs = smB[bb];
-        const uint16_t* As = smA[bb];
-        bf16x8_t bfr[NP];
+    // Operand fragments of k-half ks in buffers bb: this wave's B columns
+    // (all planes) and its A rows of plane u.
+    auto load_bfr = [&](int bb, int ks, bf16x8_t (&bfr)[NP]) __attribute__((always_inline)) {
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl)
-            bfr[pl] = *reinterpret_cast<const bf16x8_t*>(Bs + pl * PS + (gw * 32 + frag_row) * LDS_ROW +
+            bfr[pl] = *reinterpret_cast<const bf16x8_t*>(smB[bb] + pl * PS + (gw * 32 + frag_row) * LDS_ROW +
                                                          ks * 16 + frag_k);
+    };
+    auto load_afr = [&](int bb, int ks, int u, bf16x8_t (&af)[TM]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = NP - 1; u >= 0; --u) {
-            bf16x8_t af[TM];
+        for (int i = 0; i < TM; ++i)
+            af[i] = *reinterpret_cast<const bf16x8_t*>(
+                smA[bb] + u * PS + (grp * GROWS + i * 32 + frag_row) * LDS_ROW + ks * 16 + frag_k);
+    };
+    // The MFMAs of one plane u of A against all planes of B (fragments
+    // already in registers), smallest band first.
+    auto mfma_u = [&](int u, const bf16x8_t (&bfr)[NP], const bf16x8_t (&af)[TM]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t*>(
-                    As + u * PS + (grp * GROWS + i * 32 + frag_row) * LDS_ROW + ks * 16 + frag_k);
+        for (int v = NP - 1; v >= 0; --v) {
+            if (u + v < NB) {
 #pragma unroll
-            for (int v = NP - 1; v >= 0; --v) {
-                if (u + v < NB) {
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-                        // B operand first: lane l then holds row l%32 of the
-                        // 32x32 block and four consecutive columns per
-                        // register group, for 16-byte stores.
-                        acc[i][u + v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[v], af[i],
-                                                                                acc[i][u + v], 0, 0, 0);
-                }
+                for (int i = 0; i < TM; ++i)
+                    // B operand first: lane l then holds row l%32 of the
+                    // 32x32 block and four consecutive columns per register
+                    // group, for 16-byte stores.
+                    acc[i][u + v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[v], af[i], acc[i][u + v], 0, 0, 0);
             }
         }
     };
 
-    // Epilogue of this wave's 64x32 block of the tile at cursor c: bands
-    // recombined smallest first, C = alpha t + beta C, accumulators cleared.
-    // Lane l holds, per 32x32 block and register group q, row l%32 and
-    // columns 8q + 4(l/32) .. +3: one 16-byte buffer store each, rows outside
-    // C given an out-of-range offset.  Tiles that cross column N, or C
-    // without 16-byte rows, store element by element.
-    auto epilogue = [&](const Cursor& c) __attribute__((always_inline)) {
+    // Epilogue of this wave's 64x32 block of the tile at w: bands recombined
+    // smallest first, C = alpha t + beta C + bias.  Lane l holds, per 32x32
+    // block and register group q, row l%32 and columns 8q + 4(l/32) .. +3:
+    // one 16-byte buffer store each, rows outside C given an out-of-range
+    // offset.  Tiles that cross column N, or C without 16-byte rows, store
+    // element by element.  SCALE: alpha != 1.  Returns whether the vector
+    // path ran: then the epilogue's last EPI_STORES vector memory operations
+    // are its stores.
+    constexpr int EPI_STORES = TM * 4;
+    auto epilogue = [&]<bool SCALE>(const TilePos& w) __attribute__((always_inline)) {
+        const int64_t n0 = (int64_t)w.tn * TILE;
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(p.C + c.m0 * p.ldc + c.n0()), (short)0, 0x7FFFFFFF, 0x00020000);
-        const int64_t rows_left = p.M - c.m0, cols_left = p.N - c.n0();
-        const bool vec_c = p.vec_b != 0 && cols_left >= TILE;   // vec_b carries C's alignment
+            const_cast<float*>(p.C + w.m0 * p.ldc + n0), (short)0, 0x7FFFFFFF, 0x00020000);
+        const int64_t cl = p.N - n0;
+        const int cols_left = cl < TILE ? (int)cl : TILE;
+        const bool vec_c = p.vec_b != 0 && cols_left == TILE;   // vec_b carries C's alignment
         const int ldc4 = (int)p.ldc * 4;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int row = grp * GROWS + i * 32 + (lane & 31);
-            const bool row_ok = row < rows_left;
+            const bool row_ok = row < w.rows;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int col = gw * 32 + 8 * q + 4 * (lane >> 5);
@@ -574,7 +652,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
                     float sum = acc[i][NB - 1][r];
 #pragma unroll
                     for (int b = NB - 2; b >= 0; --b) sum = __builtin_fmaf(sum, 0.00390625f, acc[i][b][r]);
-                    out[e] = p.alpha * sum;
+                    out[e] = SCALE ? p.alpha * sum : sum;
                 }
                 if (vec_c) {
                     const int off = row_ok ? row * ldc4 + col * 4 : (int)0x80000000;
@@ -585,7 +663,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
                         for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(p.beta, old[e], out[e]);
                     }
                     if (p.bias != nullptr) {
-                        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.bias + c.n0() + col);
+                        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.bias + n0 + col);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) out[e] = out[e] + bv[e];
                     }
@@ -594,10 +672,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         if (row_ok && col + e < cols_left) {
-                            float* cp = p.C + (c.m0 + row) * p.ldc + c.n0() + col + e;
+                            float* cp = p.C + (w.m0 + row) * p.ldc + n0 + col + e;
                             float o = out[e];
                             if (p.beta != 0.0f) o = __builtin_fmaf(p.beta, *cp, o);
-                            if (p.bias != nullptr) o = o + p.bias[c.n0() + col + e];
+                            if (p.bias != nullptr) o = o + p.bias[n0 + col + e];
                             *cp = o;
                         }
                     }
@@ -606,68 +684,126 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[i][b] = f32x16_t{};
         }
+        return vec_c;
+    };
+    const bool unit_alpha = p.alpha == 1.0f;
+    auto epilogue_any = [&](const TilePos& w) __attribute__((always_inline)) {
+        return unit_alpha ? epilogue.template operator()<false>(w) : epilogue.template operator()<true>(w);
     };
 
-    // Cursors: cm = step of the next M phase, ce = the step before it (its
-    // tile gets the epilogue when that step was the tile's last), cs = step
-    // split next, ca / cb = steps of the next A / B loads.
-    Cursor cm, ce, cs, ca, cb;
-    cm.set(p, slot);
-    ce = cm;
-    cs = cm;
-    ca = cm;
-    cb = cm;
+    // Cursors: wm = step of the next M phase, we = the step before it (its
+    // tile gets the epilogue when that step was the tile's last), ws = the
+    // step after it (split, and its B chunk loaded, in the next U phase),
+    // wa = the step of the next A load.
+    Walk wm;
+    wm.kt = 0;
+    wm.tn = slot % p.tiles_n;
+    wm.m0 = (int64_t)(slot / p.tiles_n) * TILE;
+    wm.left = my_tiles - 1;
+    walk_set_tile(wm, wc);
+    wm.kvalid = p.nk > 1 ? BK : wc.tail_k;
+    Walk ws = wm, wa = wm;
+    TilePos we{wm.m0, wm.tn, wm.rows};
     // Prologue: B chunk of step 0; FP32 A rows of steps 0 and 1; split of
     // step 0 into plane buffer 0.
-    if (grp == 1) copy_b(cb, 0);
-    cb.next(p, G);
-    copy_a32(ca, 0);
-    ca.next(p, G);
-    copy_a32(ca, 1);
-    ca.next(p, G);
+    if (grp == 1) copy_b_rounds(ws, 0, 0, B_ROUNDS);
+    copy_a32(wa, 0);
+    walk_next(wa, wc);
+    copy_a32(wa, 1);
+    walk_next(wa, wc);
     wait_vmcnt<0>();
     {
         f32x4_t v0[A_ROUNDS];
-        load_rows(cs, 0, v0);
+        load_rows(ws, 0, v0);
         split_rows(v0, 0);
     }
-    cs.next(p, G);
+    walk_next(ws, wc);
     __syncthreads();
     if (grp == 1) __builtin_amdgcn_s_barrier();   // group 1 runs one phase behind group 0
 
+    // Vector memory operations complete in issue order, so each U phase
+    // issues its loads before the epilogue's stores, and the waits below let
+    // up to EPI_STORES stores stay in flight into the next phase.  An
+    // epilogue that loads (beta != 0: C; a bias) runs before the loads
+    // instead: the compiler's waits for its own loads would also wait for
+    // the direct loads issued before them.
+    const bool reads_c = p.beta != 0.0f || p.bias != nullptr;
+    bool epi = false;       // U(s) runs the epilogue of step s-1's tile
+    bool stores = false;    // the last U phase ended with EPI_STORES stores
     for (int s = 0; s < total; ++s) {
         const int b = s & 1;
         // ---- U(s).  The A rows of step s+1 were loaded in U(s-1) (or the
-        // prologue) into staging b^1.
-        wait_vmcnt<0>();
+        // prologue) into staging b^1; only that U phase's stores, issued
+        // after them, may still be in flight.
+        if (stores)
+            wait_vmcnt<EPI_STORES>();
+        else
+            wait_vmcnt<0>();
         f32x4_t sv[A_ROUNDS];
-        load_rows(cs, b ^ 1, sv);
-        if (s > 0 && ce.kt == p.nk - 1) epilogue(ce);
-        if (grp == 1) copy_b(cb, b ^ 1);
-        cb.next(p, G);
-        copy_a32(ca, b);   // staging b held step s, split in U(s-1)
-        ca.next(p, G);
+        load_rows(ws, b ^ 1, sv);
+        if (epi && reads_c) epilogue_any(we);
+        if (grp == 1) copy_b_rounds(ws, b ^ 1, 0, B_ROUNDS);   // B(s-1)'s buffer, last read by M(s-1)
+        copy_a32(wa, b);   // staging b held step s, split in U(s-1)
+        stores = epi && !reads_c && epilogue_any(we);
         split_rows(sv, b ^ 1);   // plane buffer b^1 was last read by M(s-1)
-        cs.next(p, G);
+        // The first fragments of M(s) are read before the barrier where they
+        // are already published: this group's A planes (split in U(s-1),
+        // published by the barrier that ended M(s-1)) and, for group 1 only,
+        // B chunk b (group 1 waited for it before that barrier; group 0's
+        // U(s) runs before it).
+        bf16x8_t bfr0[NP], atop0[TM];
+        load_afr(b, 0, NP - 1, atop0);
+        if (grp == 1) load_bfr(b, 0, bfr0);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();   // the split's writes drain during M(s)
         __builtin_amdgcn_sched_barrier(0);
-        // ---- M(s) on plane buffer b (split in U(s-1)) and B chunk b.
-        mfma_half(b, 0);
-        mfma_half(b, 1);
-        ce = cm;
-        cm.next(p, G);
+        if (grp == 0) load_bfr(b, 0, bfr0);
+        // ---- M(s) on plane buffer b (split in U(s-1)) and B chunk b, and
+        // the cursor advances for U(s+1).  The MFMAs run in 2 NP groups,
+        // (k-half, A plane u) = (0, NP-1) .. (0, 0), (1, NP-1) .. (1, 0); the
+        // fragments of each group are read while the group before it issues
+        // (the first group's before the barrier above).
+        {
+            bf16x8_t bq[2][NP], aq[2][TM];
+#pragma unroll
+            for (int pl = 0; pl < NP; ++pl) bq[0][pl] = bfr0[pl];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) aq[0][i] = atop0[i];
+#pragma unroll
+            for (int g = 0; g < 2 * NP; ++g) {
+                const int half = g / NP, u = NP - 1 - g % NP;
+                if (g + 1 < 2 * NP) {
+                    const int nhalf = (g + 1) / NP, nu = NP - 1 - (g + 1) % NP;
+                    if (nu == NP - 1) load_bfr(b, nhalf, bq[nhalf]);
+                    load_afr(b, nhalf, nu, aq[(g + 1) & 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_u(u, bq[half], aq[g & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        epi = wm.kt == p.nk - 1;
+        we = TilePos{wm.m0, wm.tn, wm.rows};
+        walk_next(wm, wc);
+        walk_next(ws, wc);
+        walk_next(wa, wc);
         // Before the next barrier: this thread's split writes of U(s) are
         // complete (the group reads them in M(s+1)); group 1's B chunk of
         // step s+1 has landed (group 0 reads it in M(s+1)), its A load of
-        // U(s) (the last A_ROUNDS issued) may still be in flight.
+        // U(s) and the epilogue's stores, issued after it, may still be in
+        // flight.
         wait_lgkmcnt0();
-        if (grp == 1) wait_vmcnt<A_ROUNDS>();
+        if (grp == 1) {
+            if (stores)
+                wait_vmcnt<A_ROUNDS + EPI_STORES>();
+            else
+                wait_vmcnt<A_ROUNDS>();
+        }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     }
-    epilogue(ce);
+    epilogue_any(we);
     wait_vmcnt<0>();   // no direct load may still be writing LDS when the workgroup ends
     if (grp == 0) __builtin_amdgcn_s_barrier();   // matches group 1's extra barrier
 }
