@@ -7,7 +7,8 @@ this package fails if the library has not been built, and every call raises
 :class:`EmuError` on a non-success status.
 
 Low-level entry points mirror the C ABI one to one (pointers are ints):
-:func:`emu_sgemm`, :func:`emu_split_bf16x3`, :func:`emu_sgemm_select`,
+:func:`emu_sgemm`, :func:`emu_sgemm_bias`, :func:`emu_sgemm_ex`,
+:func:`emu_split_bf16x3`, :func:`emu_sgemm_select`, :func:`emu_sgemm_ksplit`,
 :func:`emu_status_string`, :func:`emu_abi_version`.  :func:`sgemm` and
 :func:`split_bf16x3` accept torch tensors.
 
@@ -32,8 +33,8 @@ STATUS_NOT_SUPPORTED = 2
 STATUS_LAUNCH_FAILED = 3
 
 # C functions declared in include/emu_sgemm.h
-EXPORTS = ("emu_sgemm", "emu_sgemm_bias", "emu_split_bf16x3", "emu_sgemm_select",
-           "emu_status_string", "emu_abi_version")
+EXPORTS = ("emu_sgemm", "emu_sgemm_bias", "emu_sgemm_ex", "emu_split_bf16x3", "emu_sgemm_select",
+           "emu_sgemm_ksplit", "emu_status_string", "emu_abi_version")
 
 
 class EmuError(RuntimeError):
@@ -64,6 +65,12 @@ _lib.emu_sgemm.restype = ctypes.c_int
 _lib.emu_sgemm_bias.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, _vp,
                                 _i64, _vp, _i64, ctypes.c_float, _vp, _i64, _vp, ctypes.c_int, _vp]
 _lib.emu_sgemm_bias.restype = ctypes.c_int
+_lib.emu_sgemm_ex.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, _vp,
+                              _i64, _vp, _i64, ctypes.c_float, _vp, _i64, _vp, ctypes.c_int,
+                              ctypes.c_int, _vp]
+_lib.emu_sgemm_ex.restype = ctypes.c_int
+_lib.emu_sgemm_ksplit.argtypes = [_i64, _i64, _i64, ctypes.POINTER(ctypes.c_int)]
+_lib.emu_sgemm_ksplit.restype = ctypes.c_int
 _lib.emu_split_bf16x3.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp]
 _lib.emu_split_bf16x3.restype = ctypes.c_int
 _lib.emu_sgemm_select.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64,
@@ -104,6 +111,21 @@ def emu_sgemm_bias(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
     return int(_lib.emu_sgemm_bias(int(transA), int(transB), int(M), int(N), int(K), float(alpha),
                                    A or None, int(lda), B or None, int(ldb), float(beta), C or None,
                                    int(ldc), bias or None, _mode(mode), stream or None))
+
+
+def emu_sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, mode,
+                 ksplit, stream) -> int:
+    """Raw call; returns the status code (pointers and stream are ints)."""
+    return int(_lib.emu_sgemm_ex(int(transA), int(transB), int(M), int(N), int(K), float(alpha),
+                                 A or None, int(lda), B or None, int(ldb), float(beta), C or None,
+                                 int(ldc), bias or None, _mode(mode), int(ksplit), stream or None))
+
+
+def emu_sgemm_ksplit(M, N, K):
+    """(status, K split the library chooses for this shape or None)."""
+    out = ctypes.c_int(-1)
+    st = int(_lib.emu_sgemm_ksplit(int(M), int(N), int(K), ctypes.byref(out)))
+    return st, (out.value if st == STATUS_SUCCESS else None)
 
 
 def emu_split_bf16x3(x, n, hi, mid, lo, stream) -> int:
@@ -149,9 +171,11 @@ def _ld(x):
 
 
 def sgemm(a, b, mode="BF16X9", trans_a=False, trans_b=False, alpha=1.0, beta=0.0, c=None,
-          stream=None, bias=None):
+          stream=None, bias=None, ksplit=None):
     """C = alpha * op(a) @ op(b) + beta * c (+ bias[j] on every row) through
-    ``emu_sgemm`` (``emu_sgemm_bias`` when ``bias`` is given).
+    ``emu_sgemm`` (``emu_sgemm_bias`` when ``bias`` is given, ``emu_sgemm_ex``
+    when ``ksplit`` is given: 0 = the library's choice, S >= 1 = exactly S
+    K segments).
 
     ``a``/``b`` are the stored (row-major) matrices; ``trans_*`` select op().
     Returns ``c`` (allocated when None).  Asynchronous on ``stream``
@@ -172,6 +196,18 @@ def sgemm(a, b, mode="BF16X9", trans_a=False, trans_b=False, alpha=1.0, beta=0.0
         _check_matrix(c, "c")
         if tuple(c.shape) != (M, N):
             raise ValueError(f"c must be {M}x{N}")
+    if bias is not None and (not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32
+                             or not bias.is_cuda or bias.dim() != 1 or bias.shape[0] != N
+                             or (N > 1 and bias.stride(0) != 1)):
+        raise TypeError(f"bias must be a contiguous float32 CUDA vector of length {N}")
+    if ksplit is not None:
+        st = emu_sgemm_ex(OP_T if trans_a else OP_N, OP_T if trans_b else OP_N, M, N, K, alpha,
+                          a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), beta, c.data_ptr(), _ld(c),
+                          bias.data_ptr() if bias is not None else 0, mode, ksplit,
+                          _stream_handle(stream))
+        if st != STATUS_SUCCESS:
+            raise EmuError(st, "emu_sgemm_ex")
+        return c
     if bias is None:
         st = emu_sgemm(OP_T if trans_a else OP_N, OP_T if trans_b else OP_N, M, N, K, alpha,
                        a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), beta, c.data_ptr(), _ld(c),
@@ -179,9 +215,6 @@ def sgemm(a, b, mode="BF16X9", trans_a=False, trans_b=False, alpha=1.0, beta=0.0
         if st != STATUS_SUCCESS:
             raise EmuError(st, "emu_sgemm")
         return c
-    if (not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or not bias.is_cuda
-            or bias.dim() != 1 or bias.shape[0] != N or (N > 1 and bias.stride(0) != 1)):
-        raise TypeError(f"bias must be a contiguous float32 CUDA vector of length {N}")
     st = emu_sgemm_bias(OP_T if trans_a else OP_N, OP_T if trans_b else OP_N, M, N, K, alpha,
                         a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), beta, c.data_ptr(), _ld(c),
                         bias.data_ptr(), mode, _stream_handle(stream))
@@ -213,3 +246,11 @@ def select_mode(M, N, K, trans_a=False, trans_b=False) -> str:
     if st != STATUS_SUCCESS:
         raise EmuError(st, "emu_sgemm_select")
     return name
+
+
+def select_ksplit(M, N, K) -> int:
+    """K split the emulated modes use for this shape when A allows one."""
+    st, sp = emu_sgemm_ksplit(M, N, K)
+    if st != STATUS_SUCCESS:
+        raise EmuError(st, "emu_sgemm_ksplit")
+    return sp

@@ -94,15 +94,52 @@ constexpr double kF32Fixed = 5.288;
 constexpr double kF32Step1 = 3.033;      // us per k-step, one tile per CU
 constexpr double kF32Step2 = 5.654;      // us per k-step per round of two tiles per CU
 constexpr double kCUs = 256.0;
+// A split K (S segments of ceil(K/32)/S k-steps each) runs S times as many
+// (segment, tile) items with 1/S of the k-steps each, then a reduction
+// kernel that reads the S partial results and writes C.
+constexpr double kRedFixed = 4.0;        // us: reduction launch and tail
+constexpr double kRedBytesPerUs = 4.0e6; // bytes per us moved by the reduction
+constexpr int kMaxSplit = 8;
 
 double ceil_div(double a, double b) { return std::ceil(a / b); }
+
+double predict_x9_us(int64_t M, int64_t N, int64_t K, int split)
+{
+    const double tiles = ceil_div((double)M, 128.0) * ceil_div((double)N, 128.0);
+    const double nk = ceil_div((double)K, 32.0);
+    const double items = tiles * split;
+    const double load = items < kCUs ? items / kCUs : 1.0;
+    double t = kX9Fixed + ceil_div(items, kCUs) * (nk / split) * (kX9Step + kX9StepLoad * load);
+    if (split > 1) t += kRedFixed + (double)(split + 1) * (double)M * (double)N * 4.0 / kRedBytesPerUs;
+    return t;
+}
+
+// The K split the emulated path uses by itself (fused-A path): the divisor
+// S <= kMaxSplit of ceil(K/32) with the least predicted time, and 1 unless
+// that saves at least 5 %.
+int choose_ksplit(int64_t M, int64_t N, int64_t K)
+{
+    if (M == 0 || N == 0 || K == 0) return 1;
+    const int64_t nk = (K + 31) / 32;
+    const double t1 = predict_x9_us(M, N, K, 1);
+    int best = 1;
+    double tbest = t1;
+    for (int sp = 2; sp <= kMaxSplit && sp <= nk; ++sp) {
+        if (nk % sp != 0) continue;
+        const double t = predict_x9_us(M, N, K, sp);
+        if (t < tbest) {
+            tbest = t;
+            best = sp;
+        }
+    }
+    return tbest < 0.95 * t1 ? best : 1;
+}
 
 void predict_us(int64_t M, int64_t N, int64_t K, double& f32, double& x9)
 {
     const double tiles = ceil_div((double)M, 128.0) * ceil_div((double)N, 128.0);
     const double nk = ceil_div((double)K, 32.0);
-    const double load = tiles < kCUs ? tiles / kCUs : 1.0;
-    x9 = kX9Fixed + ceil_div(tiles, kCUs) * nk * (kX9Step + kX9StepLoad * load);
+    x9 = predict_x9_us(M, N, K, choose_ksplit(M, N, K));
     f32 = tiles <= kCUs ? kF32Fixed + nk * kF32Step1
                         : kF32Fixed + ceil_div(tiles, 2.0 * kCUs) * nk * kF32Step2;
 }
@@ -113,6 +150,11 @@ emu_mode_t select_mode(int64_t M, int64_t N, int64_t K)
     double f32, x9;
     predict_us(M, N, K, f32, x9);
     return x9 < f32 ? EMU_MODE_BF16X9 : EMU_MODE_NATIVE_F32;
+}
+
+bool emulated(emu_mode_t m)
+{
+    return m == EMU_MODE_BF16X9 || m == EMU_MODE_BF16X6 || m == EMU_MODE_BF16X3 || m == EMU_MODE_BF16X1;
 }
 
 emu_status_t from_hip(hipError_t e)
@@ -129,12 +171,14 @@ namespace {
 emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
                         float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
                         float beta, float* C, int64_t ldc, const float* bias, emu_mode_t mode,
-                        void* stream)
+                        int ksplit, void* stream)
 {
     // ---- validation: no HIP call before this block has passed ----
     if (!valid_op(transA) || !valid_op(transB)) return EMU_STATUS_INVALID_VALUE;
     if ((int)mode < (int)EMU_MODE_NATIVE_F32 || (int)mode > (int)EMU_MODE_BF16X1)
         return EMU_STATUS_INVALID_VALUE;
+    if (ksplit < 0 || (ksplit > 0 && !emulated(mode))) return EMU_STATUS_INVALID_VALUE;
+    if (ksplit > 1 && (K == 0 || ((K + 31) / 32) % ksplit != 0)) return EMU_STATUS_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return EMU_STATUS_INVALID_VALUE;
     if (lda < (transA == EMU_OP_N ? max1(K) : max1(M))) return EMU_STATUS_INVALID_VALUE;
     if (ldb < (transB == EMU_OP_N ? max1(N) : max1(K))) return EMU_STATUS_INVALID_VALUE;
@@ -150,7 +194,8 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
 
     if (K == 0 || alpha == 0.0f) return from_hip(emu::launch_scale_c(M, N, beta, C, ldc, bias, s));
 
-    if (mode == EMU_MODE_AUTO) mode = select_mode(M, N, K);
+    const bool auto_mode = mode == EMU_MODE_AUTO;
+    if (auto_mode) mode = select_mode(M, N, K);
     emu::GemmArgs g;
     g.trans_a = transA == EMU_OP_T;
     g.trans_b = transB == EMU_OP_T;
@@ -166,12 +211,18 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     g.C = C;
     g.ldc = ldc;
     g.bias = bias;
+    if (mode == EMU_MODE_NATIVE_F32) return from_hip(emu::launch_gemm_native_f32(g, dev, s));
+    const bool fused = emu::fused_a_path(g);
+    if (ksplit > 1 && !fused) return EMU_STATUS_NOT_SUPPORTED;
+    // ksplit 0: the performant policy (AUTO) may split where its cost model
+    // predicts a gain; an explicit mode computes without a split, so a row
+    // of C never depends on the other rows.
+    if (ksplit == 0) ksplit = auto_mode && fused ? choose_ksplit(M, N, K) : 1;
     switch (mode) {
-    case EMU_MODE_NATIVE_F32: return from_hip(emu::launch_gemm_native_f32(g, dev, s));
-    case EMU_MODE_BF16X9: return from_hip(emu::launch_gemm_bf16(g, 5, dev, s));
-    case EMU_MODE_BF16X6: return from_hip(emu::launch_gemm_bf16(g, 3, dev, s));
-    case EMU_MODE_BF16X3: return from_hip(emu::launch_gemm_bf16(g, 2, dev, s));
-    case EMU_MODE_BF16X1: return from_hip(emu::launch_gemm_bf16(g, 1, dev, s));
+    case EMU_MODE_BF16X9: return from_hip(emu::launch_gemm_bf16(g, 5, ksplit, dev, s));
+    case EMU_MODE_BF16X6: return from_hip(emu::launch_gemm_bf16(g, 3, ksplit, dev, s));
+    case EMU_MODE_BF16X3: return from_hip(emu::launch_gemm_bf16(g, 2, ksplit, dev, s));
+    case EMU_MODE_BF16X1: return from_hip(emu::launch_gemm_bf16(g, 1, ksplit, dev, s));
     default: return EMU_STATUS_INTERNAL;
     }
 }
@@ -193,7 +244,7 @@ const char* emu_status_string(emu_status_t status)
     }
 }
 
-int emu_abi_version(void) { return 102; }
+int emu_abi_version(void) { return 103; }
 
 emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
                               emu_mode_t* chosen)
@@ -208,7 +259,7 @@ emu_status_t emu_sgemm(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, i
                        float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
                        float beta, float* C, int64_t ldc, emu_mode_t mode, void* stream)
 {
-    return sgemm_impl(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, nullptr, mode,
+    return sgemm_impl(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, nullptr, mode, 0,
                       stream);
 }
 
@@ -217,8 +268,24 @@ emu_status_t emu_sgemm_bias(emu_op_t transA, emu_op_t transB, int64_t M, int64_t
                             float beta, float* C, int64_t ldc, const float* bias, emu_mode_t mode,
                             void* stream)
 {
-    return sgemm_impl(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, mode,
+    return sgemm_impl(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, mode, 0,
                       stream);
+}
+
+emu_status_t emu_sgemm_ex(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
+                          float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                          float beta, float* C, int64_t ldc, const float* bias, emu_mode_t mode,
+                          int ksplit, void* stream)
+{
+    return sgemm_impl(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, mode,
+                      ksplit, stream);
+}
+
+emu_status_t emu_sgemm_ksplit(int64_t M, int64_t N, int64_t K, int* ksplit)
+{
+    if (M < 0 || N < 0 || K < 0 || ksplit == nullptr) return EMU_STATUS_INVALID_VALUE;
+    *ksplit = choose_ksplit(M, N, K);
+    return EMU_STATUS_SUCCESS;
 }
 
 emu_status_t emu_split_bf16x3(const float* x, int64_t n, uint16_t* hi, uint16_t* mid,

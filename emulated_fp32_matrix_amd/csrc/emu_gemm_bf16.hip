@@ -424,29 +424,33 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 // two FP32 staging buffers (step s+2 overwrites step s, split in U(s-1)).
 // ---------------------------------------------------------------------------
 
-// A position (tile, k-step) in a workgroup's static sequence, advanced without
-// divisions: the workgroup's tiles are t0, t0 + G, t0 + 2G, ... (n fastest),
-// so each advance adds G / tiles_n tile rows and G % tiles_n tile columns.
-// Past the last step it stays put (prefetches re-read valid data).
+// A position (item, k-step) in a workgroup's static sequence, advanced
+// without divisions.  An item is one K segment of one output tile; items
+// are numbered seg * ntiles + tile (tiles n fastest), and the workgroup's
+// items are i0, i0 + G, i0 + 2G, ..., so each advance adds G / ntiles
+// segments and G % ntiles tiles, the latter as tile rows and columns.  Past
+// the last step it stays put (prefetches re-read valid data).
 struct Walk {
-    int kt;          // k-step
+    int kt;          // k-step (of the whole K)
+    int kt_end;      // one past the segment's last k-step
+    int seg;         // K segment
     int tn;          // tile column
-    int left;        // tiles after this one
+    int left;        // items after this one
     int64_t m0;      // first row
     int64_t arow;    // m0 * lda (element offset of the tile's first A row)
     int rows;        // rows of the tile inside op(A): min(M - m0, TILE)
     int kvalid;      // k of this step inside op(A): min(K - 32 kt, 32)
 };
 
-// The tile a finished step belonged to (what the epilogue needs of a Walk).
+// The item a finished step belonged to (what the epilogue needs of a Walk).
 struct TilePos {
     int64_t m0;
-    int tn, rows;
+    int tn, rows, seg;
 };
 
 struct WalkConst {
-    int nk, tiles_n, gtn, tail_k;   // tail_k: valid k of the last step
-    int64_t gm, M, lda;             // gm: rows added per advance
+    int nk, nk_item, tiles_n, gtn, gseg, tail_k;   // tail_k: valid k of the last step
+    int64_t gm, mrows, M, lda;   // gm: rows added per advance; mrows: tiles_m * TILE
 };
 
 __device__ __forceinline__ void walk_set_tile(Walk& w, const WalkConst& c)
@@ -456,25 +460,43 @@ __device__ __forceinline__ void walk_set_tile(Walk& w, const WalkConst& c)
     w.rows = r < TILE ? (int)r : TILE;
 }
 
+__device__ __forceinline__ void walk_start_segment(Walk& w, const WalkConst& c)
+{
+    w.kt = w.seg * c.nk_item;
+    w.kt_end = w.kt + c.nk_item;
+}
+
+// SPLIT: K is split into segments (otherwise seg stays 0, kt_end = nk and
+// the segment bookkeeping compiles away).
+template <bool SPLIT>
 __device__ __forceinline__ void walk_next(Walk& w, const WalkConst& c)
 {
-    if (w.kt + 1 < c.nk) {
+    if (w.kt + 1 < (SPLIT ? w.kt_end : c.nk)) {
         ++w.kt;
     } else if (w.left > 0) {
         --w.left;
-        w.kt = 0;
         w.tn += c.gtn;
         w.m0 += c.gm;
         if (w.tn >= c.tiles_n) {
             w.tn -= c.tiles_n;
             w.m0 += TILE;
         }
+        if constexpr (SPLIT) {
+            w.seg += c.gseg;
+            if (w.m0 >= c.mrows) {
+                w.m0 -= c.mrows;
+                ++w.seg;
+            }
+            walk_start_segment(w, c);
+        } else {
+            w.kt = 0;
+        }
         walk_set_tile(w, c);
     }
     w.kvalid = w.kt + 1 < c.nk ? BK : c.tail_k;
 }
 
-template <int NB>
+template <int NB, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const uint16_t* __restrict__ Wb)
 {
     constexpr int NP = NB >= 3 ? 3 : NB;
@@ -491,14 +513,19 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
 
     const int G = gridDim.x;
     const int slot = xcd_position(blockIdx.x, G);
-    const int my_tiles = (p.ntiles - slot + G - 1) / G;
-    const int total = my_tiles * p.nk;
+    const int nitems = SPLIT ? p.ntiles * p.ksplit : p.ntiles;
+    const int my_items = (nitems - slot + G - 1) / G;
+    const int total = my_items * (SPLIT ? p.nk_item : p.nk);
 
     WalkConst wc;
+    const int gtile = G % p.ntiles;   // tiles added per advance (segments: G / ntiles)
     wc.nk = p.nk;
+    wc.nk_item = p.nk_item;
     wc.tiles_n = p.tiles_n;
-    wc.gtn = G % p.tiles_n;
-    wc.gm = (int64_t)(G / p.tiles_n) * TILE;
+    wc.gtn = gtile % p.tiles_n;
+    wc.gm = (int64_t)(gtile / p.tiles_n) * TILE;
+    wc.gseg = G / p.ntiles;
+    wc.mrows = (int64_t)(p.ntiles / p.tiles_n) * TILE;
     wc.tail_k = (int)(p.K - (int64_t)(p.nk - 1) * BK);
     wc.M = p.M;
     wc.lda = p.lda;
@@ -621,23 +648,30 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         }
     };
 
-    // Epilogue of this wave's 64x32 block of the tile at w: bands recombined
-    // smallest first, C = alpha t + beta C + bias.  Lane l holds, per 32x32
-    // block and register group q, row l%32 and columns 8q + 4(l/32) .. +3:
-    // one 16-byte buffer store each, rows outside C given an out-of-range
-    // offset.  Tiles that cross column N, or C without 16-byte rows, store
-    // element by element.  SCALE: alpha != 1.  Returns whether the vector
-    // path ran: then the epilogue's last EPI_STORES vector memory operations
-    // are its stores.
+    // Epilogue of this wave's 64x32 block of the item at w: bands recombined
+    // smallest first into t, then C = alpha t + beta C + bias, or with a
+    // split K (PART) t itself into the segment's slice of the workspace.
+    // Lane l holds, per 32x32 block and register group q, row l%32 and
+    // columns 8q + 4(l/32) .. +3: one 16-byte buffer store each, rows outside
+    // C given an out-of-range offset.  Tiles that cross column N, or a
+    // destination without 16-byte rows, store element by element.  SCALE:
+    // alpha != 1.  Returns whether the vector path ran: then the epilogue's
+    // last EPI_STORES vector memory operations are its stores.
     constexpr int EPI_STORES = TM * 4;
-    auto epilogue = [&]<bool SCALE>(const TilePos& w) __attribute__((always_inline)) {
+    auto epilogue = [&]<bool SCALE, bool PART>(const TilePos& w) __attribute__((always_inline)) {
         const int64_t n0 = (int64_t)w.tn * TILE;
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(p.C + w.m0 * p.ldc + n0), (short)0, 0x7FFFFFFF, 0x00020000);
+        const int64_t ldd = PART ? p.N : p.ldc;
+        float* const dst = PART ? p.wsC + (int64_t)w.seg * p.M * p.N + w.m0 * p.N + n0
+                                : p.C + w.m0 * p.ldc + n0;
+        const float beta = PART ? 0.0f : p.beta;
+        const float* const bias = PART ? nullptr : p.bias;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, 0x7FFFFFFF, 0x00020000);
         const int64_t cl = p.N - n0;
         const int cols_left = cl < TILE ? (int)cl : TILE;
-        const bool vec_c = p.vec_b != 0 && cols_left == TILE;   // vec_b carries C's alignment
-        const int ldc4 = (int)p.ldc * 4;
+        // vec_b / vec_ws carry the destination's (and the bias') alignment
+        const bool vec_c = (PART ? p.vec_ws : p.vec_b) != 0 && cols_left == TILE;
+        const int ldd4 = (int)ldd * 4;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int row = grp * GROWS + i * 32 + (lane & 31);
@@ -655,15 +689,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
                     out[e] = SCALE ? p.alpha * sum : sum;
                 }
                 if (vec_c) {
-                    const int off = row_ok ? row * ldc4 + col * 4 : (int)0x80000000;
-                    if (p.beta != 0.0f) {
+                    const int off = row_ok ? row * ldd4 + col * 4 : (int)0x80000000;
+                    if (beta != 0.0f) {
                         const f32x4_t old = __builtin_bit_cast(
                             f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(p.beta, old[e], out[e]);
+                        for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(beta, old[e], out[e]);
                     }
-                    if (p.bias != nullptr) {
-                        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.bias + n0 + col);
+                    if (bias != nullptr) {
+                        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(bias + n0 + col);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) out[e] = out[e] + bv[e];
                     }
@@ -672,10 +706,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         if (row_ok && col + e < cols_left) {
-                            float* cp = p.C + (w.m0 + row) * p.ldc + n0 + col + e;
+                            float* cp = dst + row * ldd + col + e;
                             float o = out[e];
-                            if (p.beta != 0.0f) o = __builtin_fmaf(p.beta, *cp, o);
-                            if (p.bias != nullptr) o = o + p.bias[n0 + col + e];
+                            if (beta != 0.0f) o = __builtin_fmaf(beta, *cp, o);
+                            if (bias != nullptr) o = o + bias[n0 + col + e];
                             *cp = o;
                         }
                     }
@@ -688,7 +722,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     };
     const bool unit_alpha = p.alpha == 1.0f;
     auto epilogue_any = [&](const TilePos& w) __attribute__((always_inline)) {
-        return unit_alpha ? epilogue.template operator()<false>(w) : epilogue.template operator()<true>(w);
+        if constexpr (SPLIT)
+            return epilogue.template operator()<false, true>(w);
+        else
+            return unit_alpha ? epilogue.template operator()<false, false>(w)
+                              : epilogue.template operator()<true, false>(w);
     };
 
     // Cursors: wm = step of the next M phase, we = the step before it (its
@@ -696,28 +734,32 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     // step after it (split, and its B chunk loaded, in the next U phase),
     // wa = the step of the next A load.
     Walk wm;
-    wm.kt = 0;
-    wm.tn = slot % p.tiles_n;
-    wm.m0 = (int64_t)(slot / p.tiles_n) * TILE;
-    wm.left = my_tiles - 1;
+    {
+        const int tile0 = SPLIT ? slot % p.ntiles : slot;
+        wm.seg = SPLIT ? slot / p.ntiles : 0;
+        wm.tn = tile0 % p.tiles_n;
+        wm.m0 = (int64_t)(tile0 / p.tiles_n) * TILE;
+    }
+    wm.left = my_items - 1;
+    walk_start_segment(wm, wc);
     walk_set_tile(wm, wc);
-    wm.kvalid = p.nk > 1 ? BK : wc.tail_k;
+    wm.kvalid = wm.kt + 1 < p.nk ? BK : wc.tail_k;
     Walk ws = wm, wa = wm;
-    TilePos we{wm.m0, wm.tn, wm.rows};
+    TilePos we{wm.m0, wm.tn, wm.rows, wm.seg};
     // Prologue: B chunk of step 0; FP32 A rows of steps 0 and 1; split of
     // step 0 into plane buffer 0.
     if (grp == 1) copy_b_rounds(ws, 0, 0, B_ROUNDS);
     copy_a32(wa, 0);
-    walk_next(wa, wc);
+    walk_next<SPLIT>(wa, wc);
     copy_a32(wa, 1);
-    walk_next(wa, wc);
+    walk_next<SPLIT>(wa, wc);
     wait_vmcnt<0>();
     {
         f32x4_t v0[A_ROUNDS];
         load_rows(ws, 0, v0);
         split_rows(v0, 0);
     }
-    walk_next(ws, wc);
+    walk_next<SPLIT>(ws, wc);
     __syncthreads();
     if (grp == 1) __builtin_amdgcn_s_barrier();   // group 1 runs one phase behind group 0
 
@@ -727,7 +769,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     // epilogue that loads (beta != 0: C; a bias) runs before the loads
     // instead: the compiler's waits for its own loads would also wait for
     // the direct loads issued before them.
-    const bool reads_c = p.beta != 0.0f || p.bias != nullptr;
+    const bool reads_c = !SPLIT && (p.beta != 0.0f || p.bias != nullptr);
     bool epi = false;       // U(s) runs the epilogue of step s-1's tile
     bool stores = false;    // the last U phase ended with EPI_STORES stores
     for (int s = 0; s < total; ++s) {
@@ -782,11 +824,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        epi = wm.kt == p.nk - 1;
-        we = TilePos{wm.m0, wm.tn, wm.rows};
-        walk_next(wm, wc);
-        walk_next(ws, wc);
-        walk_next(wa, wc);
+        epi = wm.kt == (SPLIT ? wm.kt_end : p.nk) - 1;
+        we = TilePos{wm.m0, wm.tn, wm.rows, wm.seg};
+        walk_next<SPLIT>(wm, wc);
+        walk_next<SPLIT>(ws, wc);
+        walk_next<SPLIT>(wa, wc);
         // Before the next barrier: this thread's split writes of U(s) are
         // complete (the group reads them in M(s+1)); group 1's B chunk of
         // step s+1 has landed (group 0 reads it in M(s+1)), its A load of
@@ -808,6 +850,61 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     if (grp == 0) __builtin_amdgcn_s_barrier();   // matches group 1's extra barrier
 }
 
+// ---------------------------------------------------------------------------
+// Reduction of a split K: C = alpha (t_0 + t_1 + ... + t_{S-1}) + beta C
+// + bias, the segments' results added in segment order, each step one FP32
+// operation (C not read when beta == 0).  ws holds S slices of M x N (leading
+// dimension N).  Threads walk rows (blockIdx.y, strided) and 4-column groups
+// (VEC: 16-byte loads and stores; N % 4 == 0, C rows and bias 16-byte
+// aligned).
+// ---------------------------------------------------------------------------
+template <bool VEC>
+__global__ void ksplit_reduce_kernel(const float* __restrict__ ws, int S, int64_t M, int64_t N,
+                                     float alpha, float beta, float* C, int64_t ldc,
+                                     const float* __restrict__ bias)
+{
+    const int64_t groups = (N + 3) / 4;
+    const int64_t slice = M * N;
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= groups) return;
+    const int64_t j0 = g * 4;
+    for (int64_t i = blockIdx.y; i < M; i += gridDim.y) {
+        const float* w = ws + i * N + j0;
+        float* c = C + i * ldc + j0;
+        if (VEC) {
+            f32x4_t t = *reinterpret_cast<const f32x4_t*>(w);
+            for (int sg = 1; sg < S; ++sg) {
+                const f32x4_t u = *reinterpret_cast<const f32x4_t*>(w + sg * slice);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] = t[e] + u[e];
+            }
+            f32x4_t out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = alpha * t[e];
+            if (beta != 0.0f) {
+                const f32x4_t old = *reinterpret_cast<const f32x4_t*>(c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(beta, old[e], out[e]);
+            }
+            if (bias != nullptr) {
+                const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(bias + j0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = out[e] + bv[e];
+            }
+            *reinterpret_cast<f32x4_t*>(c) = out;
+        } else {
+            for (int e = 0; e < 4 && j0 + e < N; ++e) {
+                float t = w[e];
+                for (int sg = 1; sg < S; ++sg) t = t + w[sg * slice + e];
+                float o = alpha * t;
+                if (beta != 0.0f) o = __builtin_fmaf(beta, c[e], o);
+                if (bias != nullptr) o = o + bias[j0 + e];
+                c[e] = o;
+            }
+        }
+    }
+}
+
 int grid_for(int64_t work)
 {
     int64_t blocks = (work + 255) / 256;
@@ -823,8 +920,10 @@ hipError_t launch_main(const Params& p, bool fused, int grid, const uint16_t* Wb
                        const uint16_t* Wa, hipStream_t s)
 {
     constexpr int NT = ShapeMain::NT;
-    if (fused)
-        hipLaunchKernelGGL((gemm_bf16_pp_kernel<NB>), dim3(grid), dim3(512), 0, s, p, Wb);
+    if (fused && p.ksplit > 1)
+        hipLaunchKernelGGL((gemm_bf16_pp_kernel<NB, true>), dim3(grid), dim3(512), 0, s, p, Wb);
+    else if (fused)
+        hipLaunchKernelGGL((gemm_bf16_pp_kernel<NB, false>), dim3(grid), dim3(512), 0, s, p, Wb);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<ShapeMain, NB, false>), dim3(grid), dim3(NT), 0, s, p, Wb, Wa);
     return hipGetLastError();
@@ -848,7 +947,15 @@ hipError_t launch_presplit(int np, const float* X, int64_t ld, bool kc, int64_t 
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev,
+bool fused_a_path(const GemmArgs& g)
+{
+    // k-contiguous, 16-byte aligned rows whose every 16-byte group lies
+    // inside the row, and 32-bit direct-load offsets
+    return !g.trans_a && ((uintptr_t)g.A & 15u) == 0 && (g.lda & 3) == 0 && (g.K & 3) == 0 &&
+           (int64_t)TILE * g.lda * 4 < ((int64_t)1 << 32);
+}
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const DeviceInfo& dev,
                             hipStream_t stream)
 {
     if (nbands != 5 && nbands != 3 && nbands != 2 && nbands != 1) return hipErrorInvalidValue;
@@ -858,6 +965,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev
     const int64_t lim = (int64_t)1 << 31;
     if (tiles_m * tiles_n >= lim || tiles_m * tiles_n * nk >= lim || tiles_n * nk >= lim ||
         tiles_m * nk >= lim)
+        return hipErrorInvalidValue;
+    const bool fused = fused_a_path(g);
+    if (ksplit < 1 || nk % ksplit != 0 || (ksplit > 1 && !fused) ||
+        tiles_m * tiles_n * ksplit >= lim)
         return hipErrorInvalidValue;
 
     Params p{};
@@ -876,39 +987,56 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev
     p.tiles_n = (int)tiles_n;
     p.ntiles = (int)(tiles_m * tiles_n);
     p.nk = (int)nk;
-    // Fused split of A: k-contiguous, 16-byte aligned rows whose every
-    // 16-byte group lies inside the row, and 32-bit direct-load offsets.
-    const bool fused = !g.trans_a && ((uintptr_t)g.A & 15u) == 0 && (g.lda & 3) == 0 &&
-                       (g.K & 3) == 0 && (int64_t)TILE * g.lda * 4 < ((int64_t)1 << 32);
+    p.ksplit = ksplit;
+    p.nk_item = (int)(nk / ksplit);
     p.vec_a = fused ? 1 : 0;
     // (emulated kernels) C rows allow 16-byte stores at 16-byte aligned
     // columns, and the bias (if any) 16-byte loads there
     p.vec_b = (((uintptr_t)g.C & 15u) == 0 && (g.ldc & 3) == 0 &&
                (g.bias == nullptr || ((uintptr_t)g.bias & 15u) == 0) &&
                (int64_t)TILE * g.ldc * 4 < ((int64_t)1 << 31)) ? 1 : 0;
+    p.vec_ws = ((g.N & 3) == 0 && (int64_t)TILE * g.N * 4 < ((int64_t)1 << 31)) ? 1 : 0;
 
     const int np = nbands >= 3 ? 3 : nbands;
     const size_t bytes_b = (size_t)(tiles_n * nk * chunk_elems(np)) * sizeof(uint16_t);
     const size_t bytes_a = fused ? 0 : (size_t)(tiles_m * nk * chunk_elems(np)) * sizeof(uint16_t);
-    uint16_t* ws = nullptr;
+    const size_t bytes_c = ksplit > 1 ? (size_t)ksplit * (size_t)g.M * (size_t)g.N * sizeof(float) : 0;
+    char* ws = nullptr;
     hipError_t e = dev.pool != nullptr
-                       ? hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), bytes_b + bytes_a, dev.pool, stream)
-                       : hipMallocAsync(reinterpret_cast<void**>(&ws), bytes_b + bytes_a, stream);
+                       ? hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), bytes_b + bytes_a + bytes_c, dev.pool, stream)
+                       : hipMallocAsync(reinterpret_cast<void**>(&ws), bytes_b + bytes_a + bytes_c, stream);
     if (e != hipSuccess) return hipErrorOutOfMemory;
-    uint16_t* Wb = ws;
-    uint16_t* Wa = fused ? nullptr : ws + bytes_b / sizeof(uint16_t);
+    // all three parts start at multiples of 16 bytes (a chunk is NP x 10,240 bytes)
+    uint16_t* Wb = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* Wa = fused ? nullptr : reinterpret_cast<uint16_t*>(ws + bytes_b);
+    p.wsC = ksplit > 1 ? reinterpret_cast<float*>(ws + bytes_b + bytes_a) : nullptr;
 
     e = launch_presplit(np, g.B, g.ldb, g.trans_b, g.N, g.K, (int)tiles_n, (int)nk, Wb, stream);
     if (e == hipSuccess && !fused)
         e = launch_presplit(np, g.A, g.lda, !g.trans_a, g.M, g.K, (int)tiles_m, (int)nk, Wa, stream);
     if (e == hipSuccess) {
-        const int grid = p.ntiles < dev.num_cu ? p.ntiles : dev.num_cu;
+        const int64_t items = (int64_t)p.ntiles * ksplit;
+        const int grid = items < dev.num_cu ? (int)items : dev.num_cu;
         switch (nbands) {
         case 5: e = launch_main<5>(p, fused, grid, Wb, Wa, stream); break;
         case 3: e = launch_main<3>(p, fused, grid, Wb, Wa, stream); break;
         case 2: e = launch_main<2>(p, fused, grid, Wb, Wa, stream); break;
         default: e = launch_main<1>(p, fused, grid, Wb, Wa, stream); break;
         }
+    }
+    if (e == hipSuccess && ksplit > 1) {
+        const int64_t groups = (g.N + 3) / 4;
+        const int bx = (int)((groups + 255) / 256);
+        const int by = (int)(g.M < 4096 ? g.M : 4096);
+        const bool vec = (g.N & 3) == 0 && ((uintptr_t)g.C & 15u) == 0 && (g.ldc & 3) == 0 &&
+                         (g.bias == nullptr || ((uintptr_t)g.bias & 15u) == 0);
+        if (vec)
+            hipLaunchKernelGGL(ksplit_reduce_kernel<true>, dim3(bx, by), dim3(256), 0, stream, p.wsC,
+                               ksplit, g.M, g.N, g.alpha, g.beta, g.C, g.ldc, g.bias);
+        else
+            hipLaunchKernelGGL(ksplit_reduce_kernel<false>, dim3(bx, by), dim3(256), 0, stream, p.wsC,
+                               ksplit, g.M, g.N, g.alpha, g.beta, g.C, g.ldc, g.bias);
+        e = hipGetLastError();
     }
     const hipError_t ef = hipFreeAsync(ws, stream);
     return e != hipSuccess ? e : ef;

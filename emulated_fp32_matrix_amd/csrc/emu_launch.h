@@ -30,8 +30,12 @@ struct DeviceInfo {
 // workspaces go back to the device at the stream's next synchronisation.
 constexpr uint64_t kPoolKeepBytes = 256ull << 20;
 
-// nbands: 5 (BF16X9), 3 (BF16X6), 2 (BF16X3) or 1 (BF16X1).
-hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, const DeviceInfo& dev,
+// Whether the emulated path splits op(A) in its main kernel (k-contiguous,
+// aligned A); otherwise A is pre-split and K cannot be split.
+bool fused_a_path(const GemmArgs& g);
+// nbands: 5 (BF16X9), 3 (BF16X6), 2 (BF16X3) or 1 (BF16X1).  ksplit: K
+// segments, a divisor of ceil(K / 32), 1 unless fused_a_path(g).
+hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const DeviceInfo& dev,
                             hipStream_t stream);
 hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, hipStream_t stream);
 // C = beta * C + bias over M x N (C not read when beta == 0; bias may be null).

@@ -26,6 +26,13 @@ struct Params {
     int nk;        // k-steps per tile
     int vec_a;     // op(A) rows may be read with 16-byte loads
     int vec_b;     // op(B) columns may be read with 16-byte loads (native kernel)
+    // Split of K into ksplit equal segments of nk_item k-steps (fused-A
+    // kernel only; 1: none).  With ksplit > 1 the kernel writes each
+    // (segment, tile) result t, unscaled, to wsC[seg][M][N] (vec_ws: 16-byte
+    // stores allowed there) and a reduction kernel forms C.
+    int ksplit, nk_item;
+    float* wsC;
+    int vec_ws;
 };
 
 // Bijection on [0, G): hardware workgroup id -> position in the tile list.

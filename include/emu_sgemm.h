@@ -93,7 +93,12 @@ typedef enum {
  * BF16 (Figure 1's "three scaled BF16 components").  Products with piece
  * indices u + v = j are accumulated in FP32 band j; the bands kept (5, 3, 2
  * or 1) are recombined smallest first, t = S_{n-1}, t = S_j + 2^-8 t, and then
- * C = alpha * t + beta * C.
+ * C = alpha * t + beta * C.  In EMU_MODE_AUTO the library chooses, per shape,
+ * the mode (emu_sgemm_select) and, for an emulated mode, possibly a split of
+ * K into segments (emu_sgemm_ksplit, emu_sgemm_ex): then t is the sum, in
+ * segment order, of the segments' t.  So in AUTO a row of C may differ in its
+ * last bits between shapes; in an explicit mode it never depends on the
+ * other rows.  Every result is deterministic for a given shape.
  *
  * Semantics follow BLAS SGEMM:
  *   - M == 0 or N == 0: nothing is done.
@@ -138,6 +143,54 @@ emu_status_t emu_sgemm_bias(emu_op_t transA, emu_op_t transB, int64_t M, int64_t
                             void* stream);
 
 /*
+ * emu_sgemm_bias with an explicit split of K for the emulated modes.
+ *
+ * Small GEMMs, like those of the 192-atom system of "Unlocking Tensor Core
+ * Performance for Machine Learning Interatomic Potentials", section "BF16x9
+ * on NVIDIA Blackwell GPUs" (Figures 3 and 4: the smallest GEMM and MD-step
+ * speedups), have fewer 128 x 128 output tiles than the device has compute
+ * units.  Splitting K runs several K segments of each tile at once.  The
+ * split is this library's, not the pages'.
+ *
+ *   ksplit = 0:  as emu_sgemm_bias: with EMU_MODE_AUTO the performant policy
+ *                splits where its cost model predicts a gain (the split
+ *                emu_sgemm_ksplit reports); an explicit mode does not split;
+ *   ksplit >= 1: exactly that many segments; it must divide n = ceil(K / 32)
+ *                and needs an explicit emulated mode (BF16X9, X6, X3, X1).
+ *
+ * With S segments, segment s covers the k-steps [s n / S, (s + 1) n / S) of
+ * 32 k each.  Each segment's product t_s is formed as without a split (band
+ * accumulation, recombination), and then
+ *     C = alpha (t_0 + t_1 + ... + t_{S-1}) + beta C + bias,
+ * summed in segment order, every operation one FP32 rounding.  The result is
+ * a deterministic function of (inputs, ksplit): it does not depend on
+ * timing.  S > 1 adds S x M x N floats to the call's stream-ordered
+ * workspace.
+ *
+ * Errors: as emu_sgemm_bias; EMU_STATUS_INVALID_VALUE for ksplit < 0, for
+ * ksplit > 0 with EMU_MODE_NATIVE_F32 or EMU_MODE_AUTO, or for ksplit > 1
+ * that does not divide ceil(K / 32) (or K = 0); EMU_STATUS_NOT_SUPPORTED for
+ * ksplit > 1 when op(A) is transposed or A is not 16-byte addressable (A
+ * 16-byte aligned, lda and K multiples of 4): that path splits A into BF16
+ * pieces ahead of the GEMM and does not split K.
+ */
+emu_status_t emu_sgemm_ex(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
+                          float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                          float beta, float* C, int64_t ldc, const float* bias, emu_mode_t mode,
+                          int ksplit, void* stream);
+
+/*
+ * The K split EMU_MODE_AUTO uses for this shape when it runs the emulation and
+ * A allows a split (see emu_sgemm_ex); a caller of an explicit emulated mode
+ * may pass it to emu_sgemm_ex.  It is the divisor S <= 8 of ceil(K / 32)
+ * with the least time under the library's cost model, and 1 unless that
+ * saves at least 5 %.  A pure host function of (M, N, K): deterministic, no
+ * device access.
+ * Errors: EMU_STATUS_INVALID_VALUE for negative dimensions or a NULL ksplit.
+ */
+emu_status_t emu_sgemm_ksplit(int64_t M, int64_t N, int64_t K, int* ksplit);
+
+/*
  * The exact three-piece split on its own (Figure 1): for i < n,
  *   hi[i], mid[i], lo[i] = BF16 bit patterns of hi, mid', lo' of x[i]
  * with x[i] == hi + 2^-8 mid' + 2^-16 lo' exactly for every finite x[i].
@@ -166,8 +219,9 @@ emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64
  * codes give "EMU_STATUS_UNKNOWN".  Never NULL. */
 const char* emu_status_string(emu_status_t status);
 
-/* ABI version of this header (major * 100 + minor): 102 (1.1 added
- * emu_sgemm_bias, 1.2 EMU_MODE_BF16X1). */
+/* ABI version of this header (major * 100 + minor): 103 (1.1 added
+ * emu_sgemm_bias, 1.2 EMU_MODE_BF16X1, 1.3 emu_sgemm_ex and
+ * emu_sgemm_ksplit). */
 int emu_abi_version(void);
 
 #ifdef __cplusplus

@@ -63,8 +63,8 @@ def _load():
     lib.oracle_mfma_bf16_dot16.argtypes = [i64, vp, vp, vp, vp]
     lib.oracle_mfma_bf16_dot16.restype = None
     lib.oracle_emu_gemm_mfma.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, ctypes.c_int,
-                                         ctypes.c_float, vp, i64, vp, i64, ctypes.c_float, vp, i64,
-                                         vp, vp]
+                                         ctypes.c_int, ctypes.c_float, vp, i64, vp, i64,
+                                         ctypes.c_float, vp, i64, vp, vp]
     lib.oracle_emu_gemm_mfma.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -208,10 +208,12 @@ def mfma_bf16_dot16(acc, a_bits, b_bits) -> np.ndarray:
 
 
 def emu_gemm_mfma(a, b, mode="BF16X9", trans_a=False, trans_b=False, alpha=1.0, beta=0.0,
-                  c=None, bias=None) -> np.ndarray:
+                  c=None, bias=None, ksplit=1) -> np.ndarray:
     """The emulated GEMM as the GPU kernels evaluate it, bit for bit: the
     band model with every band accumulated by the kernels' sequence of
-    matrix instructions under the matrix-unit model (float32 M x N)."""
+    matrix instructions under the matrix-unit model (float32 M x N).
+    ``ksplit`` = S > 1 (dividing ceil(K/32)): K in S segments, each
+    segment's recombined result t_s, summed in segment order."""
     nb = NBANDS[mode] if isinstance(mode, str) else int(mode)
     a = _f32(a)
     b = _f32(b)
@@ -224,7 +226,7 @@ def emu_gemm_mfma(a, b, mode="BF16X9", trans_a=False, trans_b=False, alpha=1.0, 
     else:
         cp, ldc = None, max(N, 1)
     bias = _bias(bias, N)
-    _load().oracle_emu_gemm_mfma(int(trans_a), int(trans_b), M, N, K, nb, float(alpha), _ptr(a),
+    _load().oracle_emu_gemm_mfma(int(trans_a), int(trans_b), M, N, K, nb, int(ksplit), float(alpha), _ptr(a),
                                  a.shape[1], _ptr(b), b.shape[1], float(beta), cp, ldc,
                                  _ptr(bias) if bias is not None else None, _ptr(out))
     return out

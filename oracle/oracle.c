@@ -438,16 +438,24 @@ void oracle_mfma_bf16_dot16(int64_t n, const float* acc, const uint16_t* a, cons
  *   then t = S[nbands-1], t = fma(t, 2^-8, S[b]) for b = nbands-2 .. 0,
  *   r = alpha * t, r = fma(beta, C, r) if beta != 0, r = r + bias[j] if a
  *   bias is given -- each step one FP32 operation.
+ * With ksplit = S > 1 (S dividing n = ceil(K/32)) the k-steps form S
+ * segments of n/S steps; each segment's S[] start at zero and give their own
+ * t_s as above, and t = t_0, t = t + t_s for s = 1 .. S-1 (one FP32 add each)
+ * before r = alpha * t.  ksplit <= 1 (or not dividing n) is no split.
  * out is M x N, leading dimension N.
  */
 void oracle_emu_gemm_mfma(int transA, int transB, int64_t M, int64_t N, int64_t K, int nbands,
-                          float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
-                          float beta, const float* C, int64_t ldc, const float* bias, float* out)
+                          int ksplit, float alpha, const float* A, int64_t lda, const float* B,
+                          int64_t ldb, float beta, const float* C, int64_t ldc, const float* bias,
+                          float* out)
 {
     if (nbands < 1) nbands = 1;
     if (nbands > 5) nbands = 5;
     const int np = nbands >= 3 ? 3 : nbands;
     const int64_t Kp = (K + 31) / 32 * 32;
+    const int64_t nsteps = Kp / 32;
+    if (ksplit < 1 || nsteps == 0 || nsteps % ksplit != 0) ksplit = 1;
+    const int64_t seg_len = nsteps / ksplit * 32;   /* k per segment */
     /* pieces as BF16 bits: Ah[(i*Kp + k)*3 + u], Bh[(j*Kp + k)*3 + v] */
     uint16_t* Ah = (uint16_t*)calloc((size_t)(M > 0 ? M : 1) * (size_t)(Kp > 0 ? Kp : 1) * 3, 2);
     uint16_t* Bh = (uint16_t*)calloc((size_t)(N > 0 ? N : 1) * (size_t)(Kp > 0 ? Kp : 1) * 3, 2);
@@ -472,24 +480,28 @@ void oracle_emu_gemm_mfma(int transA, int transB, int64_t M, int64_t N, int64_t 
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < M; ++i) {
         for (int64_t j = 0; j < N; ++j) {
-            float S[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-            for (int64_t k0 = 0; k0 < Kp; k0 += 16) {
-                for (int u = np - 1; u >= 0; --u)
-                    for (int v = np - 1; v >= 0; --v) {
-                        if (u + v >= nbands) continue;
-                        uint16_t a16[16], b16[16];
-                        for (int e = 0; e < 16; ++e) {
-                            a16[e] = Ah[(i * Kp + k0 + e) * 3 + u];
-                            b16[e] = Bh[(j * Kp + k0 + e) * 3 + v];
+            float t = 0.0f;
+            for (int seg = 0; seg < ksplit; ++seg) {
+                float S[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+                for (int64_t k0 = seg * seg_len; k0 < (seg + 1) * seg_len; k0 += 16) {
+                    for (int u = np - 1; u >= 0; --u)
+                        for (int v = np - 1; v >= 0; --v) {
+                            if (u + v >= nbands) continue;
+                            uint16_t a16[16], b16[16];
+                            for (int e = 0; e < 16; ++e) {
+                                a16[e] = Ah[(i * Kp + k0 + e) * 3 + u];
+                                b16[e] = Bh[(j * Kp + k0 + e) * 3 + v];
+                            }
+                            float acc = S[u + v];
+                            acc = oracle_mfma_bf16_pass(acc, a16, b16, 8);
+                            acc = oracle_mfma_bf16_pass(acc, a16 + 8, b16 + 8, 8);
+                            S[u + v] = acc;
                         }
-                        float acc = S[u + v];
-                        acc = oracle_mfma_bf16_pass(acc, a16, b16, 8);
-                        acc = oracle_mfma_bf16_pass(acc, a16 + 8, b16 + 8, 8);
-                        S[u + v] = acc;
-                    }
+                }
+                float ts = S[nbands - 1];
+                for (int bb = nbands - 2; bb >= 0; --bb) ts = fmaf(ts, 0.00390625f, S[bb]);
+                t = seg == 0 ? ts : t + ts;
             }
-            float t = S[nbands - 1];
-            for (int bb = nbands - 2; bb >= 0; --bb) t = fmaf(t, 0.00390625f, S[bb]);
             float r = alpha * t;
             if (beta != 0.0f) r = fmaf(beta, C[i * ldc + j], r);
             if (bias) r = r + bias[j];

@@ -45,7 +45,7 @@ def test_status_strings_and_version():
     assert emu.emu_status_string(2) == "EMU_STATUS_NOT_SUPPORTED"
     assert emu.emu_status_string(3) == "EMU_STATUS_LAUNCH_FAILED"
     assert emu.emu_status_string(99) == "EMU_STATUS_UNKNOWN"
-    assert emu.emu_abi_version() == 102
+    assert emu.emu_abi_version() == 103
 
 
 FAKE = 0x1000  # never dereferenced: validation fails (or returns) before any HIP call
@@ -89,6 +89,37 @@ def test_bias_entry_point_invalid_arguments_rejected(args):
                 beta=0.0, C=FAKE, ldc=6, bias=FAKE, mode=1, stream=0)
     call.update(args)
     assert emu.emu_sgemm_bias(**call) == emu.STATUS_INVALID_VALUE
+
+
+@pytest.mark.parametrize("args", [
+    dict(ksplit=-1),
+    dict(ksplit=2, mode=0),     # a split needs an emulated mode: not NATIVE_F32
+    dict(ksplit=2, mode=4),     # nor AUTO
+    dict(ksplit=1, mode=0),
+    dict(ksplit=3),             # K = 64: 2 k-steps, 3 does not divide them
+    dict(ksplit=4),
+    dict(ksplit=2, K=0, lda=1, ldb=6),   # nothing to split
+    dict(transA=2), dict(mode=6), dict(M=-1), dict(lda=7), dict(C=0),
+])
+def test_split_entry_point_invalid_arguments_rejected(args):
+    call = dict(transA=0, transB=0, M=10, N=6, K=64, alpha=1.0, A=FAKE, lda=64, B=FAKE, ldb=6,
+                beta=0.0, C=FAKE, ldc=6, bias=0, mode=1, ksplit=2, stream=0)
+    call.update(args)
+    assert emu.emu_sgemm_ex(**call) == emu.STATUS_INVALID_VALUE
+
+
+def test_ksplit_choice_is_pure_and_follows_the_cost_model():
+    """emu_sgemm_ksplit: no device access; 1 for outputs with many tiles;
+    a divisor of the k-steps, at most 8, for few tiles and a long K."""
+    assert emu.emu_sgemm_ksplit(-1, 4, 4)[0] == emu.STATUS_INVALID_VALUE
+    for M, N, K in [(552960, 768, 256), (552960, 256, 768), (4096, 4096, 4096), (0, 5, 5),
+                    (5, 5, 0)]:
+        assert emu.select_ksplit(M, N, K) == 1, (M, N, K)
+    for M, N, K in [(6144, 256, 768), (2048, 256, 4096), (1024, 512, 8192)]:
+        S = emu.select_ksplit(M, N, K)
+        nk = -(-K // 32)
+        assert 1 < S <= 8 and nk % S == 0, (M, N, K, S)
+        assert all(emu.select_ksplit(M, N, K) == S for _ in range(3))
 
 
 def test_empty_shapes_return_before_touching_the_device():

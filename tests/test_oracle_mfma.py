@@ -242,3 +242,44 @@ def test_gemm_mfma_epilogue():
     want = (r + bias[None, :]).astype(np.float32)
     got = oracle.emu_gemm_mfma(a, b, "BF16X9", alpha=0.75, beta=-1.25, c=c, bias=bias)
     assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------ split K
+
+@pytest.mark.parametrize("M,N,K,S", [(17, 23, 256, 2), (9, 31, 256, 8), (12, 20, 200, 7),
+                                     (30, 8, 96, 3), (5, 6, 64, 2)])
+def test_gemm_mfma_ksplit_is_segment_sum(M, N, K, S):
+    """K split into S segments of n/S k-steps (32 k each, the last one holding
+    the ragged tail): the result is the segments' own emulated products
+    (unsplit oracle calls on the K slices) added in segment order in FP32,
+    then alpha and the bias."""
+    rng = np.random.default_rng(M + N + K + S)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    b = rng.standard_normal((K, N)).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    nk = -(-K // 32)
+    L = nk // S * 32
+    t = None
+    for s in range(S):
+        ks = slice(s * L, min(K, (s + 1) * L))
+        ts = oracle.emu_gemm_mfma(np.ascontiguousarray(a[:, ks]), np.ascontiguousarray(b[ks, :]),
+                                  "BF16X9")
+        t = ts if t is None else (t + ts).astype(np.float32)
+    want = ((np.float32(0.5) * t).astype(np.float32) + bias[None, :]).astype(np.float32)
+    got = oracle.emu_gemm_mfma(a, b, "BF16X9", alpha=0.5, bias=bias, ksplit=S)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_gemm_mfma_ksplit_closed_forms():
+    rng = np.random.default_rng(11)
+    a = rng.integers(-100, 101, (20, 128)).astype(np.float32)
+    b = rng.integers(-100, 101, (128, 24)).astype(np.float32)
+    exact = a.astype(np.int64) @ b.astype(np.int64)
+    x = (rng.standard_normal((16, 128)) * 2.0 ** rng.integers(-20, 20, (16, 128))).astype(np.float32)
+    for S in (1, 2, 4):
+        assert np.array_equal(oracle.emu_gemm_mfma(a, b, "BF16X9", ksplit=S).astype(np.int64), exact)
+        assert np.array_equal(oracle.emu_gemm_mfma(x, np.eye(128, dtype=np.float32), "BF16X9",
+                                                   ksplit=S), x)
+    # a split that does not divide the k-steps is no split
+    assert np.array_equal(oracle.emu_gemm_mfma(x, np.eye(128, dtype=np.float32), "BF16X9",
+                                               ksplit=3), x)
