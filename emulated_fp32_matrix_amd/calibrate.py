@@ -9,7 +9,8 @@ Device time, not wall time: each batch of calls is queued behind a GPU spin
 launch cost, and a pair of HIP events around the batch times the device
 work of one call (for BF16X9: the B pre-split and the main kernel).
 
-    python3 -m emulated_fp32_matrix_amd.calibrate [--fit] [--out table.json]
+    python3 -m emulated_fp32_matrix_amd.calibrate [--fit [--markdown]] [--out table.json]
+    python3 -m emulated_fp32_matrix_amd.calibrate --table table.json --fit --markdown
 
 Prints one line per shape; with --fit also the least-squares constants of
 the model in csrc/emu_api.hip and how often the model picks the faster mode.
@@ -84,16 +85,19 @@ def measure(modes=("NATIVE_F32", "BF16X9")):
     return rows
 
 
-# ---- the cost model (same form as select_mode in csrc/emu_api.hip) ----
-PARAMS = ("x9_fixed", "x9_b", "x9_step", "x9_step_load", "f32_fixed", "f32_step1", "f32_step2")
+# ---- the cost model (same form as predict_x9_us / predict_us in csrc/emu_api.hip) ----
+PARAMS = ("x9_fixed", "x9_step_part", "x9_step_full", "f32_fixed", "f32_step1", "f32_step2")
 
 
 def predict(M, N, K, p):
+    """(native, BF16X9 unsplit) predicted device time in microseconds: the
+    emulated kernel runs ceil(tiles / 256) rounds of nk k-steps, each step
+    costing x9_step_full once every CU has a tile and x9_step_part before;
+    the native kernel one tile per CU up to 256 tiles, two beyond."""
     tiles = math.ceil(M / 128) * math.ceil(N / 128)
     nk = math.ceil(K / 32)
-    load = min(1.0, tiles / 256)
-    x9 = (p["x9_fixed"] + p["x9_b"] * (nk * 32) * (math.ceil(N / 128) * 128) / 1e6 +
-          math.ceil(tiles / 256) * nk * (p["x9_step"] + p["x9_step_load"] * load))
+    step = p["x9_step_full"] if tiles >= 256 else p["x9_step_part"]
+    x9 = p["x9_fixed"] + math.ceil(tiles / 256) * nk * step
     if tiles <= 256:
         f32 = p["f32_fixed"] + nk * p["f32_step1"]
     else:
@@ -104,8 +108,8 @@ def predict(M, N, K, p):
 def fit(rows):
     from scipy.optimize import minimize
 
-    start = dict(x9_fixed=12.0, x9_b=0.3, x9_step=1.3, x9_step_load=0.7, f32_fixed=6.0,
-                 f32_step1=2.9, f32_step2=5.1)
+    start = dict(x9_fixed=22.0, x9_step_part=1.2, x9_step_full=2.1, f32_fixed=10.0,
+                 f32_step1=3.0, f32_step2=5.9)
 
     def loss(v):
         p = dict(zip(PARAMS, v))
@@ -118,7 +122,7 @@ def fit(rows):
         return e
 
     res = minimize(loss, [start[k] for k in PARAMS], method="Nelder-Mead",
-                   options=dict(maxiter=40000, xatol=1e-5, fatol=1e-8))
+                   options=dict(maxiter=80000, xatol=1e-7, fatol=1e-10))
     p = dict(zip(PARAMS, res.x))
     wrong, worst = 0, 1.0
     for r in rows:
@@ -130,11 +134,28 @@ def fit(rows):
     return p, wrong, worst
 
 
+def markdown(rows, p):
+    """The measured table with the model's predictions and choices."""
+    out = ["| shape | M | N | K | NATIVE_F32 us | BF16X9 us | native / X9 | model native | model X9 "
+           "| AUTO picks | picks the faster |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        f32, x9 = predict(r["M"], r["N"], r["K"], p)
+        nat, emu = r["us_NATIVE_F32"], r["us_BF16X9"]
+        pick = "BF16X9" if x9 < f32 else "NATIVE_F32"
+        got = emu if pick == "BF16X9" else nat
+        ok = "yes" if got <= min(nat, emu) else f"no ({got / min(nat, emu):.3f}x)"
+        out.append(f"| {r['label']} | {r['M']} | {r['N']} | {r['K']} | {nat:.1f} | {emu:.1f} | "
+                   f"{nat / emu:.2f} | {f32:.1f} | {x9:.1f} | {pick} | {ok} |")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--fit", action="store_true")
     ap.add_argument("--out", default=None, help="write the measured table as JSON")
     ap.add_argument("--table", default=None, help="fit a table written earlier instead of measuring")
+    ap.add_argument("--markdown", action="store_true", help="with --fit: print the table with the "
+                    "model's predictions and choices")
     args = ap.parse_args()
     rows = json.load(open(args.table)) if args.table else measure()
     if args.out:
@@ -144,6 +165,8 @@ def main():
         print("fitted (microseconds): " + ", ".join(f"{k}={v:.4f}" for k, v in p.items()))
         print(f"model picks the slower mode on {wrong} of {len(rows)} shapes; worst ratio to the "
               f"faster mode {worst:.3f}")
+        if args.markdown:
+            print(markdown(rows, p))
 
 
 if __name__ == "__main__":

@@ -79,24 +79,26 @@ int64_t max1(int64_t v) { return v > 1 ? v : 1; }
 // Cost model of one call on MI355X: predicted device time in microseconds,
 // including the B pre-split and the stream-ordered workspace of the emulated
 // path.  Its form follows the kernels: 128x128 output tiles, K in steps of
-// 32; the emulated kernel keeps one tile per CU (256 at a time) and its step
-// time grows with the fraction of CUs busy; the native kernel runs one tile
-// per CU up to 256 tiles and two per CU beyond.  The constants are a
-// least-squares fit (log error) to device times measured with
-// emulated_fp32_matrix_amd/calibrate.py over 67 shapes: the MLIP layer
-// stacks, squares 128..8192, skinny shapes and a K sweep.  On those shapes the
-// choice is the faster mode in 60 of 67 cases and within 8 % of it in the
-// rest.
-constexpr double kX9Fixed = 21.76;       // us: pre-split launch, workspace, pipeline fill
-constexpr double kX9Step = 1.012;        // us per k-step per tile round, idle chip
-constexpr double kX9StepLoad = 1.016;    // us added per k-step when all CUs are busy
-constexpr double kF32Fixed = 5.288;
-constexpr double kF32Step1 = 3.033;      // us per k-step, one tile per CU
-constexpr double kF32Step2 = 5.654;      // us per k-step per round of two tiles per CU
+// 32; the emulated kernel keeps one (tile or K-segment) item per CU (256 at
+// a time), and a k-step costs more once every CU is busy (the clock is then
+// power-limited); the native kernel runs one tile per CU up to 256 tiles and
+// two per CU beyond.  The constants are a least-squares fit (log error) to
+// device times measured with emulated_fp32_matrix_amd/calibrate.py over 67
+// shapes: the MLIP layer stacks, squares 128..8192, skinny shapes and a K
+// sweep.  On those shapes the choice is the faster mode in 65 of 67 cases
+// and within 12 % of it in the other two.
+constexpr double kX9Fixed = 22.97;       // us: pre-split launch, workspace, pipeline fill
+constexpr double kX9StepPart = 1.245;    // us per k-step per round while some CUs are idle
+constexpr double kX9StepFull = 2.087;    // us per k-step per round with every CU busy
+constexpr double kF32Fixed = 10.505;
+constexpr double kF32Step1 = 3.067;      // us per k-step, one tile per CU
+constexpr double kF32Step2 = 5.922;      // us per k-step per round of two tiles per CU
 constexpr double kCUs = 256.0;
 // A split K (S segments of ceil(K/32)/S k-steps each) runs S times as many
 // (segment, tile) items with 1/S of the k-steps each, then a reduction
-// kernel that reads the S partial results and writes C.
+// kernel that reads the S partial results and writes C.  With these two
+// constants the split chosen below is the fastest measured one on 14 of the
+// 16 GEMMs of the two 6,144-row stacks, within 7 % on the other two.
 constexpr double kRedFixed = 4.0;        // us: reduction launch and tail
 constexpr double kRedBytesPerUs = 4.0e6; // bytes per us moved by the reduction
 constexpr int kMaxSplit = 8;
@@ -108,8 +110,8 @@ double predict_x9_us(int64_t M, int64_t N, int64_t K, int split)
     const double tiles = ceil_div((double)M, 128.0) * ceil_div((double)N, 128.0);
     const double nk = ceil_div((double)K, 32.0);
     const double items = tiles * split;
-    const double load = items < kCUs ? items / kCUs : 1.0;
-    double t = kX9Fixed + ceil_div(items, kCUs) * (nk / split) * (kX9Step + kX9StepLoad * load);
+    const double step = items >= kCUs ? kX9StepFull : kX9StepPart;
+    double t = kX9Fixed + ceil_div(items, kCUs) * (nk / split) * step;
     if (split > 1) t += kRedFixed + (double)(split + 1) * (double)M * (double)N * 4.0 / kRedBytesPerUs;
     return t;
 }

@@ -12,7 +12,13 @@ Per stack and policy it reports the step time two ways:
   device - the same 8 calls queued behind a GPU spin, so the events time the
            device work alone (what a captured graph or a busy stream sees).
 
+With --ksplit-sweep it instead times every GEMM of the stacks in BF16X9
+with each K split S (a divisor of ceil(K/32), S <= 8; emu_sgemm_ex), beside
+the split the AUTO policy picks (emu_sgemm_ksplit) and native FP32 (device
+time, calls queued behind a GPU spin, median of 5 runs of 20 calls).
+
     python3 -m emulated_fp32_matrix_amd.policies [--stacks 2 3 4] [--json out.json]
+    python3 -m emulated_fp32_matrix_amd.policies --ksplit-sweep --stacks 2 4 [--json out.json]
 """
 from __future__ import annotations
 
@@ -55,8 +61,9 @@ def time_stack(stack, reps=5):
         for g, a, b, c in tensors:
             emu.sgemm(a, b, mode=mode, trans_a=g.trans_a, trans_b=g.trans_b, c=c)
 
+    splits = {g.name: emu.select_ksplit(g.M, g.N, g.K) for g in gemms}
     out = {"stack": stack, "name": synth.CONFIG_NAMES[stack], "gflop": flops / 1e9,
-           "auto_choice": choice, "policies": {}}
+           "auto_choice": choice, "auto_ksplit": splits, "policies": {}}
     for pol, mode in POLICIES.items():
         for _ in range(3):
             step(mode)
@@ -84,13 +91,70 @@ def time_stack(stack, reps=5):
     return out
 
 
+def _device_us(fn, calls=20, reps=5):
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        torch.cuda._sleep(20_000_000)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / calls)
+    return statistics.median(ts)
+
+
+def ksplit_sweep(stack):
+    import torch
+
+    import emulated_fp32_matrix_amd as emu
+
+    synth = _synth()
+    dev = torch.device("cuda:0")
+    rows = []
+    for g in synth.gemms(stack):
+        a = torch.from_numpy(synth.make_a(g)).to(dev)
+        b = torch.from_numpy(synth.make_b(g)).to(dev)
+        c = torch.empty((g.M, g.N), dtype=torch.float32, device=dev)
+        nk = -(-g.K // 32)
+        times = {}
+        for S in [s for s in range(1, 9) if nk % s == 0]:
+            times[S] = _device_us(lambda: emu.sgemm(a, b, mode="BF16X9", trans_a=g.trans_a,
+                                                    trans_b=g.trans_b, c=c, ksplit=S))
+        native = _device_us(lambda: emu.sgemm(a, b, mode="NATIVE_F32", trans_a=g.trans_a,
+                                              trans_b=g.trans_b, c=c))
+        auto = emu.select_ksplit(g.M, g.N, g.K)
+        best = min(times, key=times.get)
+        rows.append({"gemm": g.name, "M": g.M, "N": g.N, "K": g.K, "auto_ksplit": auto,
+                     "best_ksplit": best, "x9_us": {str(k): round(v, 1) for k, v in times.items()},
+                     "native_us": round(native, 1)})
+        print(f"stack {stack} {g.name:8s} {g.M}x{g.N}x{g.K}: auto S={auto} best S={best}  " +
+              "  ".join(f"S{k} {v:6.1f}" for k, v in times.items()) + f"  native {native:6.1f} us",
+              flush=True)
+        del a, b, c
+    torch.cuda.empty_cache()
+    return {"stack": stack, "name": synth.CONFIG_NAMES[stack], "gemms": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--stacks", type=int, nargs="+", default=[2, 4, 3])
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--json", default=None)
+    ap.add_argument("--ksplit-sweep", action="store_true")
     args = ap.parse_args()
-    res = [time_stack(s, args.reps) for s in args.stacks]
+    if args.ksplit_sweep:
+        res = [ksplit_sweep(s) for s in args.stacks]
+    else:
+        res = [time_stack(s, args.reps) for s in args.stacks]
     if args.json:
         json.dump(res, open(args.json, "w"), indent=1)
 
