@@ -20,14 +20,50 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
+// One stream's workspace on a device (see stream_workspace).
+struct WsEntry {
+    bool used = false;
+    hipStream_t stream = nullptr;
+    void* ptr = nullptr;
+    size_t size = 0;
+    uint64_t last = 0;
+};
+constexpr int kWsEntries = 16;
+
 struct DeviceSlot {
     bool ready = false;
     bool supported = false;
     emu::DeviceInfo info{};
+    WsEntry ws[kWsEntries];
+    uint64_t tick = 0;
 };
 
 std::mutex g_dev_mutex;
 DeviceSlot g_dev[kMaxDevices];
+
+// A memory pool on device `dev` that keeps up to kPoolKeepBytes of freed
+// memory mapped; null (and no error left behind) if one cannot be made.
+hipMemPool_t make_pool(int dev)
+{
+    hipMemPoolProps pp;
+    memset(&pp, 0, sizeof(pp));
+    pp.allocType = hipMemAllocationTypePinned;
+    pp.handleTypes = hipMemHandleTypeNone;
+    pp.location.type = hipMemLocationTypeDevice;
+    pp.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &pp) != hipSuccess) {
+        (void)hipGetLastError();   // our failure must not surface in a later launch check
+        return nullptr;
+    }
+    uint64_t keep = emu::kPoolKeepBytes;
+    if (hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep) != hipSuccess) {
+        (void)hipMemPoolDestroy(pool);
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    return pool;
+}
 
 // Returns true and fills `info` when the current device is a gfx950.
 bool current_device(emu::DeviceInfo& info)
@@ -41,35 +77,69 @@ bool current_device(emu::DeviceInfo& info)
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
         s.supported = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
         s.info.num_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
-        // A pool of our own that keeps freed workspace mapped (up to
-        // kPoolKeepBytes), so that a call's stream-ordered workspace is not
-        // mapped and unmapped every time; without it the device's default
-        // pool is used.
-        s.info.pool = nullptr;
-        hipMemPoolProps pp;
-        memset(&pp, 0, sizeof(pp));
-        pp.allocType = hipMemAllocationTypePinned;
-        pp.handleTypes = hipMemHandleTypeNone;
-        pp.location.type = hipMemLocationTypeDevice;
-        pp.location.id = dev;
-        hipMemPool_t pool = nullptr;
-        if (s.supported) {
-            if (hipMemPoolCreate(&pool, &pp) == hipSuccess) {
-                uint64_t keep = emu::kPoolKeepBytes;
-                if (hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep) == hipSuccess) {
-                    s.info.pool = pool;
-                } else {
-                    (void)hipMemPoolDestroy(pool);
-                    (void)hipGetLastError();   // our failure must not surface in a later launch check
-                }
-            } else {
-                (void)hipGetLastError();
-            }
-        }
+        // A pool of our own for the stream workspaces (keeping freed memory
+        // mapped up to kPoolKeepBytes); without it the device's default pool
+        // is used.
+        s.info.device = dev;
+        s.info.pool = s.supported ? make_pool(dev) : nullptr;
         s.ready = true;
     }
     info = s.info;
     return s.supported;
+}
+
+// A device workspace of at least `bytes` for a call on stream `st`.  Each
+// stream keeps one grow-only buffer, used only by calls on that stream and
+// so only in its order: calls on different streams never share one, and a
+// stream's buffer is reused call after call without allocating (a
+// stream-ordered allocation and free costs every call several microseconds
+// of device time, and more when the sizes vary).  Growing frees the old
+// buffer in the stream's order.  With kWsEntries streams in use, the least
+// recently used one's buffer is released with hipFree, which waits for the
+// device.  The buffers live until the process ends.
+hipError_t stream_workspace(const emu::DeviceInfo& info, hipStream_t st, size_t bytes, void** out)
+{
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    DeviceSlot& d = g_dev[info.device];
+    ++d.tick;
+    WsEntry* e = nullptr;
+    for (WsEntry& w : d.ws)
+        if (w.used && w.stream == st) e = &w;
+    if (e == nullptr) {
+        for (WsEntry& w : d.ws)
+            if (!w.used && e == nullptr) e = &w;
+        if (e == nullptr) {
+            e = &d.ws[0];
+            for (WsEntry& w : d.ws)
+                if (w.last < e->last) e = &w;
+            if (e->ptr != nullptr && hipFree(e->ptr) != hipSuccess) return hipErrorUnknown;
+            *e = WsEntry{};
+        }
+        e->used = true;
+        e->stream = st;
+    }
+    e->last = d.tick;
+    if (e->size < bytes) {
+        size_t want = e->size + e->size / 2;
+        if (want < bytes) want = bytes;
+        want = (want + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);   // whole MiB
+        if (e->ptr != nullptr) {
+            if (hipFreeAsync(e->ptr, st) != hipSuccess) return hipErrorUnknown;
+            e->ptr = nullptr;
+            e->size = 0;
+        }
+        void* p = nullptr;
+        const hipError_t r = info.pool != nullptr ? hipMallocFromPoolAsync(&p, want, info.pool, st)
+                                                  : hipMallocAsync(&p, want, st);
+        if (r != hipSuccess) {
+            (void)hipGetLastError();   // reported as EMU_STATUS_ALLOC_FAILED, not by a later launch
+            return hipErrorOutOfMemory;
+        }
+        e->ptr = p;
+        e->size = want;
+    }
+    *out = e->ptr;
+    return hipSuccess;
 }
 
 bool valid_op(int op) { return op == EMU_OP_N || op == EMU_OP_T; }
@@ -220,13 +290,18 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     // predicts a gain; an explicit mode computes without a split, so a row
     // of C never depends on the other rows.
     if (ksplit == 0) ksplit = auto_mode && fused ? choose_ksplit(M, N, K) : 1;
+    int nbands;
     switch (mode) {
-    case EMU_MODE_BF16X9: return from_hip(emu::launch_gemm_bf16(g, 5, ksplit, dev, s));
-    case EMU_MODE_BF16X6: return from_hip(emu::launch_gemm_bf16(g, 3, ksplit, dev, s));
-    case EMU_MODE_BF16X3: return from_hip(emu::launch_gemm_bf16(g, 2, ksplit, dev, s));
-    case EMU_MODE_BF16X1: return from_hip(emu::launch_gemm_bf16(g, 1, ksplit, dev, s));
+    case EMU_MODE_BF16X9: nbands = 5; break;
+    case EMU_MODE_BF16X6: nbands = 3; break;
+    case EMU_MODE_BF16X3: nbands = 2; break;
+    case EMU_MODE_BF16X1: nbands = 1; break;
     default: return EMU_STATUS_INTERNAL;
     }
+    void* ws = nullptr;
+    if (stream_workspace(dev, s, emu::gemm_bf16_workspace_bytes(g, nbands, ksplit), &ws) != hipSuccess)
+        return EMU_STATUS_ALLOC_FAILED;
+    return from_hip(emu::launch_gemm_bf16(g, nbands, ksplit, dev, ws, s));
 }
 
 }  // namespace

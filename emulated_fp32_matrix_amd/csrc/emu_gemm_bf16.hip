@@ -955,8 +955,41 @@ bool fused_a_path(const GemmArgs& g)
            (int64_t)TILE * g.lda * 4 < ((int64_t)1 << 32);
 }
 
+namespace {
+
+// The workspace's parts: pre-split B (and A when not fused), then the split-K
+// partial results, each starting at a multiple of 256 bytes.
+struct WsLayout {
+    size_t b, a, c;   // offsets
+    size_t total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const GemmArgs& g, int nbands, int ksplit)
+{
+    const int64_t tiles_m = (g.M + TILE - 1) / TILE;
+    const int64_t tiles_n = (g.N + TILE - 1) / TILE;
+    const int64_t nk = (g.K + BK - 1) / BK;
+    const int np = nbands >= 3 ? 3 : nbands;
+    const bool fused = fused_a_path(g);
+    WsLayout w;
+    w.b = 0;
+    w.a = round256((size_t)(tiles_n * nk * chunk_elems(np)) * sizeof(uint16_t));
+    w.c = w.a + (fused ? 0 : round256((size_t)(tiles_m * nk * chunk_elems(np)) * sizeof(uint16_t)));
+    w.total = w.c + (ksplit > 1 ? round256((size_t)ksplit * (size_t)g.M * (size_t)g.N * sizeof(float)) : 0);
+    return w;
+}
+
+}  // namespace
+
+size_t gemm_bf16_workspace_bytes(const GemmArgs& g, int nbands, int ksplit)
+{
+    return ws_layout(g, nbands, ksplit).total;
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const DeviceInfo& dev,
-                            hipStream_t stream)
+                            void* workspace, hipStream_t stream)
 {
     if (nbands != 5 && nbands != 3 && nbands != 2 && nbands != 1) return hipErrorInvalidValue;
     const int64_t tiles_m = (g.M + TILE - 1) / TILE;
@@ -968,7 +1001,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const Dev
         return hipErrorInvalidValue;
     const bool fused = fused_a_path(g);
     if (ksplit < 1 || nk % ksplit != 0 || (ksplit > 1 && !fused) ||
-        tiles_m * tiles_n * ksplit >= lim)
+        tiles_m * tiles_n * ksplit >= lim || workspace == nullptr)
         return hipErrorInvalidValue;
 
     Params p{};
@@ -998,20 +1031,13 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const Dev
     p.vec_ws = ((g.N & 3) == 0 && (int64_t)TILE * g.N * 4 < ((int64_t)1 << 31)) ? 1 : 0;
 
     const int np = nbands >= 3 ? 3 : nbands;
-    const size_t bytes_b = (size_t)(tiles_n * nk * chunk_elems(np)) * sizeof(uint16_t);
-    const size_t bytes_a = fused ? 0 : (size_t)(tiles_m * nk * chunk_elems(np)) * sizeof(uint16_t);
-    const size_t bytes_c = ksplit > 1 ? (size_t)ksplit * (size_t)g.M * (size_t)g.N * sizeof(float) : 0;
-    char* ws = nullptr;
-    hipError_t e = dev.pool != nullptr
-                       ? hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), bytes_b + bytes_a + bytes_c, dev.pool, stream)
-                       : hipMallocAsync(reinterpret_cast<void**>(&ws), bytes_b + bytes_a + bytes_c, stream);
-    if (e != hipSuccess) return hipErrorOutOfMemory;
-    // all three parts start at multiples of 16 bytes (a chunk is NP x 10,240 bytes)
-    uint16_t* Wb = reinterpret_cast<uint16_t*>(ws);
-    uint16_t* Wa = fused ? nullptr : reinterpret_cast<uint16_t*>(ws + bytes_b);
-    p.wsC = ksplit > 1 ? reinterpret_cast<float*>(ws + bytes_b + bytes_a) : nullptr;
+    const WsLayout lay = ws_layout(g, nbands, ksplit);
+    char* ws = static_cast<char*>(workspace);
+    uint16_t* Wb = reinterpret_cast<uint16_t*>(ws + lay.b);
+    uint16_t* Wa = fused ? nullptr : reinterpret_cast<uint16_t*>(ws + lay.a);
+    p.wsC = ksplit > 1 ? reinterpret_cast<float*>(ws + lay.c) : nullptr;
 
-    e = launch_presplit(np, g.B, g.ldb, g.trans_b, g.N, g.K, (int)tiles_n, (int)nk, Wb, stream);
+    hipError_t e = launch_presplit(np, g.B, g.ldb, g.trans_b, g.N, g.K, (int)tiles_n, (int)nk, Wb, stream);
     if (e == hipSuccess && !fused)
         e = launch_presplit(np, g.A, g.lda, !g.trans_a, g.M, g.K, (int)tiles_m, (int)nk, Wa, stream);
     if (e == hipSuccess) {
@@ -1038,8 +1064,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const Dev
                                ksplit, g.M, g.N, g.alpha, g.beta, g.C, g.ldc, g.bias);
         e = hipGetLastError();
     }
-    const hipError_t ef = hipFreeAsync(ws, stream);
-    return e != hipSuccess ? e : ef;
+    return e;
 }
 
 }  // namespace emu

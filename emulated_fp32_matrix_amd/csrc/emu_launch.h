@@ -22,8 +22,9 @@ struct GemmArgs {
 };
 
 struct DeviceInfo {
+    int device;          // HIP device index
     int num_cu;          // compute units of the current device
-    hipMemPool_t pool;   // library-owned pool for call workspaces (null: the device's default pool)
+    hipMemPool_t pool;   // library-owned pool for the workspaces (null: the device's default pool)
 };
 
 // Bytes of freed workspace the library's pool keeps mapped for reuse; larger
@@ -33,10 +34,13 @@ constexpr uint64_t kPoolKeepBytes = 256ull << 20;
 // Whether the emulated path splits op(A) in its main kernel (k-contiguous,
 // aligned A); otherwise A is pre-split and K cannot be split.
 bool fused_a_path(const GemmArgs& g);
-// nbands: 5 (BF16X9), 3 (BF16X6), 2 (BF16X3) or 1 (BF16X1).  ksplit: K
-// segments, a divisor of ceil(K / 32), 1 unless fused_a_path(g).
+// Device workspace the emulated path needs (bytes, a multiple of 256), and
+// the launch with it: nbands 5 (BF16X9), 3 (BF16X6), 2 (BF16X3) or 1
+// (BF16X1); ksplit K segments, a divisor of ceil(K / 32), 1 unless
+// fused_a_path(g); `workspace` 256-byte aligned, used in stream order only.
+size_t gemm_bf16_workspace_bytes(const GemmArgs& g, int nbands, int ksplit);
 hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const DeviceInfo& dev,
-                            hipStream_t stream);
+                            void* workspace, hipStream_t stream);
 hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, hipStream_t stream);
 // C = beta * C + bias over M x N (C not read when beta == 0; bias may be null).
 hipError_t launch_scale_c(int64_t M, int64_t N, float beta, float* C, int64_t ldc,

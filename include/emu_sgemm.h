@@ -24,20 +24,23 @@
  *     A column-major caller computes C^T = B^T A^T by swapping operands.
  *   - Every array pointer is device memory owned by the caller.  The library
  *     keeps no reference to it after the call returns.
- *   - Memory: emu_sgemm in the BF16X* modes takes one stream-ordered
- *     workspace for the BF16 planes of op(B), pre-split once per call (plus
- *     those of op(A) when A cannot be split inside the GEMM: transA == T,
- *     A not 16-byte aligned, or lda or K not a multiple of 4).  It is
- *     allocated on `stream` from a memory pool the library creates once per
- *     device (hipMallocFromPoolAsync; the device's default pool if creating
- *     one fails) and released with hipFreeAsync on the same stream before
- *     the call returns, so it lives exactly as long as the call's kernels.
- *     The pool keeps up to 256 MiB of freed workspace mapped for reuse
- *     until the process ends; larger workspaces are returned to the device
- *     at the stream's next synchronisation.  Size
+ *   - Memory: the BF16X* modes need a device workspace for the BF16 planes
+ *     of op(B), pre-split once per call (plus those of op(A) when A cannot
+ *     be split inside the GEMM: transA == T, A not 16-byte aligned, or lda
+ *     or K not a multiple of 4, and the partial results of a split K).  Size
  *     for B: planes * 2 bytes * ceil(N/128)*128 * ceil(K/32)*40 (3 planes,
- *     2 in BF16X3; every 32 k-values of a row padded to 40), likewise with M
- *     for A.  NATIVE_F32 and emu_split_bf16x3 allocate nothing.
+ *     2 in BF16X3, 1 in BF16X1; every 32 k-values of a row padded to 40),
+ *     likewise with M for A; S * M * N * 4 bytes for a split into S
+ *     segments.  The library keeps one workspace per (device, stream): a
+ *     buffer that grows to the largest size a call on that stream has needed
+ *     and is used only by calls on that stream, so in its order.  It is
+ *     allocated on the stream from a memory pool the library creates once
+ *     per device (hipMallocFromPoolAsync; the device's default pool if
+ *     creating one fails); growing frees the old buffer with hipFreeAsync on
+ *     the stream.  Up to 16 streams per device keep a buffer; beyond that the
+ *     least recently used one is released with hipFree, which waits for the
+ *     device.  The buffers live until the process ends.  NATIVE_F32 and
+ *     emu_split_bf16x3 allocate nothing.
  *   - stream is a hipStream_t (NULL = the null stream).  Work is enqueued on
  *     it asynchronously; errors during execution surface at the caller's
  *     next synchronisation of that stream.
@@ -80,7 +83,7 @@ typedef enum {
     EMU_STATUS_INVALID_VALUE = 1,  /* bad dimension, leading dimension, pointer or enum */
     EMU_STATUS_NOT_SUPPORTED = 2,  /* no gfx950 device current, or device query failed */
     EMU_STATUS_LAUNCH_FAILED = 3,  /* the kernel launch itself reported an error */
-    EMU_STATUS_ALLOC_FAILED = 4,   /* the stream-ordered workspace could not be allocated */
+    EMU_STATUS_ALLOC_FAILED = 4,   /* the stream's workspace could not be allocated or grown */
     EMU_STATUS_INTERNAL = 5
 } emu_status_t;
 
@@ -164,8 +167,7 @@ emu_status_t emu_sgemm_bias(emu_op_t transA, emu_op_t transB, int64_t M, int64_t
  *     C = alpha (t_0 + t_1 + ... + t_{S-1}) + beta C + bias,
  * summed in segment order, every operation one FP32 rounding.  The result is
  * a deterministic function of (inputs, ksplit): it does not depend on
- * timing.  S > 1 adds S x M x N floats to the call's stream-ordered
- * workspace.
+ * timing.  S > 1 adds S x M x N floats to the workspace.
  *
  * Errors: as emu_sgemm_bias; EMU_STATUS_INVALID_VALUE for ksplit < 0, for
  * ksplit > 0 with EMU_MODE_NATIVE_F32 or EMU_MODE_AUTO, or for ksplit > 1
