@@ -156,13 +156,13 @@ int64_t max1(int64_t v) { return v > 1 ? v : 1; }
 // device times measured with emulated_fp32_matrix_amd/calibrate.py over 67
 // shapes: the MLIP layer stacks, squares 128..8192, skinny shapes and a K
 // sweep.  On those shapes the choice is the faster mode in 65 of 67 cases
-// and within 12 % of it in the other two.
-constexpr double kX9Fixed = 22.97;       // us: pre-split launch, workspace, pipeline fill
-constexpr double kX9StepPart = 1.245;    // us per k-step per round while some CUs are idle
-constexpr double kX9StepFull = 2.087;    // us per k-step per round with every CU busy
-constexpr double kF32Fixed = 10.505;
-constexpr double kF32Step1 = 3.067;      // us per k-step, one tile per CU
-constexpr double kF32Step2 = 5.922;      // us per k-step per round of two tiles per CU
+// and within 14 % of it in the other two.
+constexpr double kX9Fixed = 11.62;       // us: pre-split launch, pipeline fill
+constexpr double kX9StepPart = 1.564;    // us per k-step per round while some CUs are idle
+constexpr double kX9StepFull = 2.113;    // us per k-step per round with every CU busy
+constexpr double kF32Fixed = 10.540;
+constexpr double kF32Step1 = 3.045;      // us per k-step, one tile per CU
+constexpr double kF32Step2 = 5.842;      // us per k-step per round of two tiles per CU
 constexpr double kCUs = 256.0;
 // A split K (S segments of ceil(K/32)/S k-steps each) runs S times as many
 // (segment, tile) items with 1/S of the k-steps each, then a reduction
