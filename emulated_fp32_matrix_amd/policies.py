@@ -19,6 +19,7 @@ time, calls queued behind a GPU spin, median of 5 runs of 20 calls).
 
     python3 -m emulated_fp32_matrix_amd.policies [--stacks 2 3 4] [--json out.json]
     python3 -m emulated_fp32_matrix_amd.policies --ksplit-sweep --stacks 2 4 [--json out.json]
+    python3 -m emulated_fp32_matrix_amd.policies --markdown out.json   # tables of a saved run
 """
 from __future__ import annotations
 
@@ -144,13 +145,64 @@ def ksplit_sweep(stack):
     return {"stack": stack, "name": synth.CONFIG_NAMES[stack], "gemms": rows}
 
 
+def _policy_markdown(res):
+    out = []
+    for r in res:
+        out.append(f"## Stack: {r['name']} ({r['gflop']:.2f} GFLOP per step)\n")
+        choice = ", ".join(f"{k} {v}" + (f" (K split {r['auto_ksplit'][k]})"
+                                          if r.get("auto_ksplit", {}).get(k, 1) > 1 else "")
+                           for k, v in r["auto_choice"].items())
+        out.append(f"AUTO's choices: {choice}\n")
+        out.append("| policy | mode | wall us | wall TFLOP/s | wall speedup | device us | device TFLOP/s "
+                   "| device speedup |\n|---|---|---|---|---|---|---|---|")
+        nat = r["policies"]["native"]
+        for name, p in r["policies"].items():
+            out.append(f"| {name} | {p['mode']} | {p['wall_us']:.1f} | {p['wall_tflops']:.1f} | "
+                       f"{nat['wall_us'] / p['wall_us']:.2f} | {p['device_us']:.1f} | "
+                       f"{p['device_tflops']:.1f} | {nat['device_us'] / p['device_us']:.2f} |")
+        out.append("")
+    return "\n".join(out)
+
+
+def _ksplit_markdown(res):
+    out = []
+    for r in res:
+        splits = sorted({int(s) for g in r["gemms"] for s in g["x9_us"]})
+        out.append(f"## {r['name']}\n")
+        out.append("| GEMM | M x N x K | tiles | " + " | ".join(f"S = {s}" for s in splits) +
+                   " | native | AUTO S | best S | AUTO vs S = 1 |")
+        out.append("|---|---|---|" + "---|" * len(splits) + "---|---|---|---|")
+        tot = {"s1": 0.0, "auto": 0.0, "best": 0.0, "native": 0.0}
+        for g in r["gemms"]:
+            t = {int(k): v for k, v in g["x9_us"].items()}
+            tiles = -(-g["M"] // 128) * -(-g["N"] // 128)
+            cells = " | ".join(f"{t[s]:.1f}" if s in t else "" for s in splits)
+            auto = t[g["auto_ksplit"]]
+            out.append(f"| {g['gemm']} | {g['M']} x {g['N']} x {g['K']} | {tiles} | {cells} | "
+                       f"{g['native_us']:.1f} | {g['auto_ksplit']} | {g['best_ksplit']} | "
+                       f"{t[1] / auto:.2f}x |")
+            tot["s1"] += t[1]
+            tot["auto"] += auto
+            tot["best"] += t[g["best_ksplit"]]
+            tot["native"] += g["native_us"]
+        out.append(f"\nStack total: S = 1 {tot['s1']:.1f} us, AUTO's split {tot['auto']:.1f} us "
+                   f"({tot['s1'] / tot['auto']:.2f}x), best split {tot['best']:.1f} us, "
+                   f"native {tot['native']:.1f} us.\n")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--stacks", type=int, nargs="+", default=[2, 4, 3])
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--json", default=None)
     ap.add_argument("--ksplit-sweep", action="store_true")
+    ap.add_argument("--markdown", default=None, help="print the tables of a JSON file written earlier")
     args = ap.parse_args()
+    if args.markdown:
+        res = json.load(open(args.markdown))
+        print(_ksplit_markdown(res) if res and "gemms" in res[0] else _policy_markdown(res))
+        return
     if args.ksplit_sweep:
         res = [ksplit_sweep(s) for s in args.stacks]
     else:
