@@ -23,6 +23,24 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// A zeroed MFMA accumulator, written as eight 64-bit moves (v_mov_b64)
+// instead of sixteen 32-bit ones: half the VALU issue slots for the clears
+// that follow every output tile.  The asm is volatile so that the moves are
+// neither merged into one shared zero register (which would then be copied)
+// nor hoisted out of the loop that reuses the accumulator.
+__device__ __forceinline__ f32x16_t zero_acc()
+{
+    typedef double f64x8_t __attribute__((ext_vector_type(8)));
+    f64x8_t z;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        double d;
+        asm volatile("v_mov_b64 %0, 0" : "=v"(d));
+        z[j] = d;
+    }
+    return __builtin_bit_cast(f32x16_t, z);
+}
+
 // Largest finite FP32 whose BF16 rounding is finite (0x7F7F7FFF): clamping
 // to it before R makes the conversion saturate exactly as R prescribes.
 __device__ __forceinline__ float bf16_sat_limit() { return __uint_as_float(0x7F7F7FFFu); }

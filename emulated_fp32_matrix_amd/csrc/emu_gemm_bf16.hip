@@ -611,12 +611,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         }
     };
 
-    // Accumulators: cleared here and by each tile's epilogue.
+    // Accumulators: cleared here and after each tile's epilogue.
     f32x16_t acc[TM][NB];
+    auto clear_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[i][b] = f32x16_t{};
+            for (int b = 0; b < NB; ++b) acc[i][b] = zero_acc();
+    };
+    clear_acc();
 
     // Operand fragments of k-half ks in buffers bb: this wave's B columns
     // (all planes) and its A rows of plane u.
@@ -715,8 +718,6 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
                     }
                 }
             }
-#pragma unroll
-            for (int b = 0; b < NB; ++b) acc[i][b] = f32x16_t{};
         }
         return vec_c;
     };
@@ -783,10 +784,17 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
             wait_vmcnt<0>();
         f32x4_t sv[A_ROUNDS];
         load_rows(ws, b ^ 1, sv);
-        if (epi && reads_c) epilogue_any(we);
+        if (epi && reads_c) {
+            epilogue_any(we);
+            clear_acc();
+        }
         if (grp == 1) copy_b_rounds(ws, b ^ 1, 0, B_ROUNDS);   // B(s-1)'s buffer, last read by M(s-1)
         copy_a32(wa, b);   // staging b held step s, split in U(s-1)
-        stores = epi && !reads_c && epilogue_any(we);
+        stores = false;
+        if (epi && !reads_c) {
+            stores = epilogue_any(we);
+            clear_acc();   // here, not in each epilogue variant: one copy of the clears
+        }
         split_rows(sv, b ^ 1);   // plane buffer b^1 was last read by M(s-1)
         // The first fragments of M(s) are read before the barrier where they
         // are already published: this group's A planes (split in U(s-1),
