@@ -40,6 +40,20 @@ namespace {
 
 constexpr int PS = TILE * LDS_ROW; // elements per plane of an LDS tile
 
+// Plane rows carry no padding.  Instead the four 16-byte chunks of row r
+// (k = 8c .. 8c+7 in chunk c) are stored in the order c ^ plane_swz(r), which
+// depends on r % 16 only.  The fragment reads of an MFMA operand (16 or 8
+// consecutive rows at one chunk per pass, 16 bytes per lane) then fall in
+// distinct banks, and the split's 8-byte writes (whole rows per pass) are
+// unaffected.  Against rows padded to 80 bytes this saves a fifth of every
+// plane's LDS space and of the B chunks' load volume.
+__host__ __device__ constexpr int plane_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Element offset of (row r, k) within one plane.
+__host__ __device__ constexpr int plane_elem(int r, int k)
+{
+    return r * LDS_ROW + ((((k >> 3) ^ plane_swz(r)) << 3) | (k & 7));
+}
+
 // Workgroup shape: NT threads; waves arranged (NT/64/WN) x WN, each owning
 // TM x TN MFMA tiles of 32x32.
 template <int NT_, int WN_, int TM_, int TN_>
@@ -55,10 +69,10 @@ __host__ __device__ constexpr int64_t chunk_elems(int np) { return (int64_t)np *
 
 // ---------------------------------------------------------------------------
 // Pre-split of an operand viewed as [rows][k] into the chunk layout
-// [tile row][k-step][plane][128][LDS_ROW].  Element (r, k) is X[r*ld + k]
-// when kc (k contiguous) and X[k*ld + r] otherwise.  One thread per (row,
-// 8-wide k group) of the padded extent; rows past `rows` and k past K are
-// zero.  The 8 padding columns of each row are not written (never read).
+// [tile row][k-step][plane][128][LDS_ROW] (chunks of a row permuted as
+// plane_elem places them).  Element (r, k) is X[r*ld + k] when kc (k
+// contiguous) and X[k*ld + r] otherwise.  One thread per (row, 8-wide k
+// group) of the padded extent; rows past `rows` and k past K are zero.
 // ---------------------------------------------------------------------------
 template <int NP>
 __global__ void presplit_kernel(const float* __restrict__ X, int64_t ld, int kc, int64_t rows,
@@ -90,7 +104,7 @@ __global__ void presplit_kernel(const float* __restrict__ X, int64_t ld, int kc,
         const int64_t tr = r / TILE, rr = r - tr * TILE;
         const int64_t kt = k0 / BK, kk = k0 - kt * BK;
         uint16_t* chunk = W + (tr * nk + kt) * chunk_elems(NP);
-        const int64_t off = rr * LDS_ROW + kk;
+        const int64_t off = plane_elem((int)rr, (int)kk);
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl)
             *reinterpret_cast<u32x4_t*>(chunk + pl * PS + off) = u32x4_t{w[0][pl], w[1][pl], w[2][pl], w[3][pl]};
@@ -206,7 +220,7 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
             uint32_t w0[NP], w1[NP];
             split_pieces<NP>(v[0], v[1], w0);
             split_pieces<NP>(v[2], v[3], w1);
-            uint16_t* dst = smA[pb] + row * LDS_ROW + skc;
+            uint16_t* dst = smA[pb] + plane_elem(row, skc);
 #pragma unroll
             for (int pl = 0; pl < NP; ++pl) *reinterpret_cast<u32x2_t*>(dst + pl * PS) = u32x2_t{w0[pl], w1[pl]};
         }
@@ -230,8 +244,7 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int col = (wn * TN + j) * 32 + frag_row;
-                bfr[pl][j] = *reinterpret_cast<const bf16x8_t*>(Bs + pl * PS + col * LDS_ROW +
-                                                                ks * 16 + frag_k);
+                bfr[pl][j] = *reinterpret_cast<const bf16x8_t*>(Bs + pl * PS + plane_elem(col, ks * 16 + frag_k));
             }
 #pragma unroll
         for (int u = NP - 1; u >= 0; --u) {
@@ -239,8 +252,7 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int row = (wm * TM + i) * 32 + frag_row;
-                af[i] = *reinterpret_cast<const bf16x8_t*>(As + u * PS + row * LDS_ROW + ks * 16 +
-                                                           frag_k);
+                af[i] = *reinterpret_cast<const bf16x8_t*>(As + u * PS + plane_elem(row, ks * 16 + frag_k));
             }
 #pragma unroll
             for (int v = NP - 1; v >= 0; --v) {
@@ -401,8 +413,8 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 // waves a 64x32 block (two 32x32 MFMA tiles).  Each group alternates two
 // kinds of phase, each closed by a workgroup barrier:
 //   U(s): reads the group's FP32 A rows of step s+1 from staging, then
-//         (while those reads are in flight) issues the direct loads of the
-//         B chunk of step s+1 (group 1 only) and of the A rows of step s+2,
+//         (while those reads are in flight) issues the direct loads of its
+//         half of the B chunk of step s+1 and of its A rows of step s+2,
 //         runs the epilogue of the tile that ended at step s-1 (its stores
 //         issued after the loads, so that waiting for the loads never waits
 //         for them), then splits the step s+1 rows into the other plane
@@ -419,9 +431,11 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 // for at the end of the next M phase, and each thread splits exactly the A
 // elements it loaded itself, so its own load-counter wait publishes them to
 // itself.
-// LDS: two plane buffers for A (each group touches only its own rows), two
-// B chunk buffers (B(s+1) is loaded while both groups may still read B(s)),
-// two FP32 staging buffers (step s+2 overwrites step s, split in U(s-1)).
+// LDS: two plane buffers for A (each group touches only its own rows),
+// three B chunk buffers (group 0 loads its half of B(s+1) in U0(s), while
+// group 1's M(s-1) still reads B(s-1) and B(s) waits for M(s)), two FP32
+// staging buffers (step s+2 overwrites step s, split in U(s-1)): 152 KB
+// with three planes.
 // ---------------------------------------------------------------------------
 
 // A position (item, k-step) in a workgroup's static sequence, advanced
@@ -503,12 +517,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     constexpr int CHUNK_BYTES = (int)chunk_elems(NP) * 2;
     constexpr int GT = 256;                                // threads per group
     constexpr int GROWS = TILE / 2;                        // A rows per group
-    constexpr int B_ROUNDS = (CHUNK_BYTES + GT * 16 - 1) / (GT * 16);
+    constexpr int B_ROUNDS = CHUNK_BYTES / (GT * 16);      // 4 KB rounds per B chunk
+    constexpr int B_HALF = B_ROUNDS / 2;                   // rounds each group copies
     constexpr int A_ROUNDS = GROWS * BK * 4 / (GT * 16);   // 16-byte loads per thread
     constexpr int TM = 2;
     static_assert(A_ROUNDS == 2 && GROWS == 2 * 32, "thread t splits rows t/8 and t/8 + 32 of its group");
+    static_assert(B_ROUNDS * GT * 16 == CHUNK_BYTES && B_HALF * 2 == B_ROUNDS, "B chunk in whole half rounds");
     __shared__ __attribute__((aligned(16))) uint16_t smA[2][chunk_elems(NP)];
-    __shared__ __attribute__((aligned(16))) uint16_t smB[2][chunk_elems(NP)];
+    __shared__ __attribute__((aligned(16))) uint16_t smB[3][chunk_elems(NP)];
     __shared__ __attribute__((aligned(16))) float stage[2][TILE * BK];
 
     const int G = gridDim.x;
@@ -569,16 +585,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
 #pragma unroll
         for (int r = 0; r < A_ROUNDS; ++r) copy_a32_round(w, sb, r);
     };
-    // Rounds [r0, r1) of the group's copy of the B chunk of step w into
-    // buffer bb: round r moves the 4 KB at 4096 r, this wave's 1 KB piece of
-    // it at 4096 r + 1024 gw (the last round may be partial).
-    auto copy_b_rounds = [&](const Walk& w, int bb, int r0, int r1) __attribute__((always_inline)) {
+    // This group's half of the B chunk of step w into buffer bb: rounds
+    // B_HALF g .. B_HALF g + B_HALF - 1, round r the 4 KB at 4096 r, this
+    // wave's 1 KB piece of it at 4096 r + 1024 gw.
+    auto copy_b_half = [&](const Walk& w, int bb) __attribute__((always_inline)) {
         const char* src = reinterpret_cast<const char*>(Wb + ((int64_t)w.tn * p.nk + w.kt) * chunk_elems(NP));
         const uint32_t dst = lds_offset(smB[bb]);
 #pragma unroll
-        for (int r = r0; r < r1; ++r) {
-            const int byte0 = (r * GT + gw * 64) * 16;
-            if (byte0 < CHUNK_BYTES) copy16_to_lds(dst + byte0, src + byte0, (uint32_t)lane * 16);
+        for (int j = 0; j < B_HALF; ++j) {
+            const int byte0 = ((grp * B_HALF + j) * GT + gw * 64) * 16;
+            copy16_to_lds(dst + byte0, src + byte0, (uint32_t)lane * 16);
         }
     };
     // The split of the group's rows of one step, in two parts: load_rows
@@ -598,14 +614,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
             }
         }
     };
+    const int split_off = plane_elem(srow0, skc);   // rows 32 apart share the chunk order
     auto split_rows = [&](const f32x4_t (&v)[A_ROUNDS], int ab) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < A_ROUNDS; ++q) {
-            const int row = srow0 + 32 * q;
             uint32_t w0[NP], w1[NP];
             split_pieces<NP>(v[q][0], v[q][1], w0);
             split_pieces<NP>(v[q][2], v[q][3], w1);
-            uint16_t* dst = smA[ab] + row * LDS_ROW + skc;
+            uint16_t* dst = smA[ab] + split_off + 32 * q * LDS_ROW;
 #pragma unroll
             for (int pl = 0; pl < NP; ++pl) *reinterpret_cast<u32x2_t*>(dst + pl * PS) = u32x2_t{w0[pl], w1[pl]};
         }
@@ -621,19 +637,22 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     };
     clear_acc();
 
-    // Operand fragments of k-half ks in buffers bb: this wave's B columns
-    // (all planes) and its A rows of plane u.
+    // Operand fragments of k-half ks: this wave's B columns (all planes) in
+    // B buffer bb and its A rows of plane u in plane buffer ab.  Fragment
+    // rows start at multiples of 32, so the lane's offset within a plane is
+    // frag_off0 (ks = 0) or frag_off1 (ks = 1) past the first row's.
+    const int frag_off0 = plane_elem(frag_row, frag_k), frag_off1 = plane_elem(frag_row, 16 + frag_k);
     auto load_bfr = [&](int bb, int ks, bf16x8_t (&bfr)[NP]) __attribute__((always_inline)) {
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl)
-            bfr[pl] = *reinterpret_cast<const bf16x8_t*>(smB[bb] + pl * PS + (gw * 32 + frag_row) * LDS_ROW +
-                                                         ks * 16 + frag_k);
+            bfr[pl] = *reinterpret_cast<const bf16x8_t*>(smB[bb] + pl * PS + gw * 32 * LDS_ROW +
+                                                         (ks ? frag_off1 : frag_off0));
     };
-    auto load_afr = [&](int bb, int ks, int u, bf16x8_t (&af)[TM]) __attribute__((always_inline)) {
+    auto load_afr = [&](int ab, int ks, int u, bf16x8_t (&af)[TM]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-            af[i] = *reinterpret_cast<const bf16x8_t*>(
-                smA[bb] + u * PS + (grp * GROWS + i * 32 + frag_row) * LDS_ROW + ks * 16 + frag_k);
+            af[i] = *reinterpret_cast<const bf16x8_t*>(smA[ab] + u * PS + (grp * GROWS + i * 32) * LDS_ROW +
+                                                       (ks ? frag_off1 : frag_off0));
     };
     // The MFMAs of one plane u of A against all planes of B (fragments
     // already in registers), smallest band first.
@@ -747,9 +766,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     wm.kvalid = wm.kt + 1 < p.nk ? BK : wc.tail_k;
     Walk ws = wm, wa = wm;
     TilePos we{wm.m0, wm.tn, wm.rows, wm.seg};
-    // Prologue: B chunk of step 0; FP32 A rows of steps 0 and 1; split of
-    // step 0 into plane buffer 0.
-    if (grp == 1) copy_b_rounds(ws, 0, 0, B_ROUNDS);
+    // Prologue: B chunk of step 0 (each group its half); FP32 A rows of
+    // steps 0 and 1; split of step 0 into plane buffer 0.
+    copy_b_half(ws, 0);
     copy_a32(wa, 0);
     walk_next<SPLIT>(wa, wc);
     copy_a32(wa, 1);
@@ -773,11 +792,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     const bool reads_c = !SPLIT && (p.beta != 0.0f || p.bias != nullptr);
     bool epi = false;       // U(s) runs the epilogue of step s-1's tile
     bool stores = false;    // the last U phase ended with EPI_STORES stores
+    int bm = 0;             // B buffer of step s: s % 3
     for (int s = 0; s < total; ++s) {
         const int b = s & 1;
+        const int bn = bm == 2 ? 0 : bm + 1;   // B buffer of step s+1
         // ---- U(s).  The A rows of step s+1 were loaded in U(s-1) (or the
-        // prologue) into staging b^1; only that U phase's stores, issued
-        // after them, may still be in flight.
+        // prologue) into staging b^1, after that phase's half of B chunk
+        // s; only that U phase's stores, issued after them, may still be in
+        // flight.
         if (stores)
             wait_vmcnt<EPI_STORES>();
         else
@@ -788,7 +810,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
             epilogue_any(we);
             clear_acc();
         }
-        if (grp == 1) copy_b_rounds(ws, b ^ 1, 0, B_ROUNDS);   // B(s-1)'s buffer, last read by M(s-1)
+        // B chunk s+1 goes to the buffer of step s-2, whose last readers,
+        // M(s-2) of both groups, ended before this phase.
+        copy_b_half(ws, bn);
         copy_a32(wa, b);   // staging b held step s, split in U(s-1)
         stores = false;
         if (epi && !reads_c) {
@@ -799,16 +823,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         // The first fragments of M(s) are read before the barrier where they
         // are already published: this group's A planes (split in U(s-1),
         // published by the barrier that ended M(s-1)) and, for group 1 only,
-        // B chunk b (group 1 waited for it before that barrier; group 0's
-        // U(s) runs before it).
+        // B chunk s (both halves had landed before the barrier that ended
+        // U0(s), which group 0's U(s) precedes).
         bf16x8_t bfr0[NP], atop0[TM];
         load_afr(b, 0, NP - 1, atop0);
-        if (grp == 1) load_bfr(b, 0, bfr0);
+        if (grp == 1) load_bfr(bm, 0, bfr0);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();   // the split's writes drain during M(s)
         __builtin_amdgcn_sched_barrier(0);
-        if (grp == 0) load_bfr(b, 0, bfr0);
-        // ---- M(s) on plane buffer b (split in U(s-1)) and B chunk b, and
+        if (grp == 0) load_bfr(bm, 0, bfr0);
+        // ---- M(s) on plane buffer b (split in U(s-1)) and B buffer bm, and
         // the cursor advances for U(s+1).  The MFMAs run in 2 NP groups,
         // (k-half, A plane u) = (0, NP-1) .. (0, 0), (1, NP-1) .. (1, 0); the
         // fragments of each group are read while the group before it issues
@@ -824,7 +848,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
                 const int half = g / NP, u = NP - 1 - g % NP;
                 if (g + 1 < 2 * NP) {
                     const int nhalf = (g + 1) / NP, nu = NP - 1 - (g + 1) % NP;
-                    if (nu == NP - 1) load_bfr(b, nhalf, bq[nhalf]);
+                    if (nu == NP - 1) load_bfr(bm, nhalf, bq[nhalf]);
                     load_afr(b, nhalf, nu, aq[(g + 1) & 1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -837,11 +861,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         walk_next<SPLIT>(wm, wc);
         walk_next<SPLIT>(ws, wc);
         walk_next<SPLIT>(wa, wc);
+        bm = bn;
         // Before the next barrier: this thread's split writes of U(s) are
-        // complete (the group reads them in M(s+1)); group 1's B chunk of
-        // step s+1 has landed (group 0 reads it in M(s+1)), its A load of
+        // complete (the group reads them in M(s+1)); group 1's half of B
+        // chunk s+1 has landed (group 0 reads it in M(s+1)), its A load of
         // U(s) and the epilogue's stores, issued after it, may still be in
-        // flight.
+        // flight.  Group 0's half landed before U0(s+1)'s own wait, which
+        // precedes the barrier that ends U0(s+1).
         wait_lgkmcnt0();
         if (grp == 1) {
             if (stores)

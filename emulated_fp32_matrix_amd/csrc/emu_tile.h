@@ -9,7 +9,7 @@ namespace emu {
 
 constexpr int BK = 32;             // k extent of one pipeline step
 constexpr int TILE = 128;          // output tile is TILE x TILE
-constexpr int LDS_ROW = BK + 8;    // bf16 elements per LDS row: 80 bytes, conflict-free 16-byte reads
+constexpr int LDS_ROW = BK;        // bf16 elements per row of an LDS plane: 64 bytes, no padding
 constexpr int LDSF_ROW = BK + 4;   // fp32 elements per LDS row (native kernel): 144 bytes
 
 // One GEMM call as the kernels see it (row-major; op(A) M x K, op(B) K x N).

@@ -28,8 +28,8 @@
  *     of op(B), pre-split once per call (plus those of op(A) when A cannot
  *     be split inside the GEMM: transA == T, A not 16-byte aligned, or lda
  *     or K not a multiple of 4, and the partial results of a split K).  Size
- *     for B: planes * 2 bytes * ceil(N/128)*128 * ceil(K/32)*40 (3 planes,
- *     2 in BF16X3, 1 in BF16X1; every 32 k-values of a row padded to 40),
+ *     for B: planes * 2 bytes * ceil(N/128)*128 * ceil(K/32)*32 (3 planes,
+ *     2 in BF16X3, 1 in BF16X1),
  *     likewise with M for A; S * M * N * 4 bytes for a split into S
  *     segments.  The library keeps one workspace per (device, stream): a
  *     buffer that grows to the largest size a call on that stream has needed
