@@ -416,26 +416,28 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 // kinds of phase, each closed by a workgroup barrier:
 //   U(s): reads the group's FP32 A rows of step s+1 from staging, then
 //         (while those reads are in flight) issues the direct loads of its
-//         half of the B chunk of step s+1 and of its A rows of step s+2,
+//         half of a B chunk (group 0: step s+1, group 1: step s+2) and of
+//         its A rows of step s+2,
 //         runs the epilogue of the tile that ended at step s-1 (its stores
 //         issued after the loads, so that waiting for the loads never waits
 //         for them), then splits the step s+1 rows into the other plane
 //         buffer;
-//   M(s): the MFMAs of step s, and the scalar bookkeeping (advancing the
-//         step cursors, precomputing addresses) for the next U phase.
+//   M(s): the MFMAs of step s, then the scalar bookkeeping (advancing the
+//         step cursors, precomputing addresses) for the next U phase, and
+//         the wait for the group's half of B loaded in U(s).
 // Group 1 starts one phase late, so U of one group runs beside M of the
 // other: on every SIMD one wave keeps the matrix unit busy while the other
 // does the vector, LDS and memory work.  Since a wave issues one instruction
 // at a time, scalar work costs issue slots in a U phase but fills idle ones
 // between the MFMAs of an M phase, which is where it is placed.  An M
 // phase's fragment reads run one group of MFMAs ahead of their use, the
-// first group's before the barrier.  The split's LDS writes are only waited
+// first group's (A and B) before the barrier.  The split's LDS writes are only waited
 // for at the end of the next M phase, and each thread splits exactly the A
 // elements it loaded itself, so its own load-counter wait publishes them to
 // itself.
 // LDS: two plane buffers for A (each group touches only its own rows),
-// three B chunk buffers (group 0 loads its half of B(s+1) in U0(s), while
-// group 1's M(s-1) still reads B(s-1) and B(s) waits for M(s)), two FP32
+// three B chunk buffers (chunks s-1 .. s+1 while group 0 loads its half of
+// s+1, s .. s+2 while group 1 loads its half of s+2), two FP32
 // staging buffers (step s+2 overwrites step s, split in U(s-1)): 152 KB
 // with three planes.
 // ---------------------------------------------------------------------------
@@ -768,8 +770,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     wm.kvalid = wm.kt + 1 < p.nk ? BK : wc.tail_k;
     Walk ws = wm, wa = wm;
     TilePos we{wm.m0, wm.tn, wm.rows, wm.seg};
-    // Prologue: B chunk of step 0 (each group its half); FP32 A rows of
-    // steps 0 and 1; split of step 0 into plane buffer 0.
+    // Prologue: B chunk of step 0 (each group its half) and group 1's half
+    // of B chunk 1; FP32 A rows of steps 0 and 1; split of step 0 into
+    // plane buffer 0.
     copy_b_half(ws, 0);
     copy_a32(wa, 0);
     walk_next<SPLIT>(wa, wc);
@@ -782,6 +785,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         split_rows(v0, 0);
     }
     walk_next<SPLIT>(ws, wc);
+    if (grp == 1) {
+        copy_b_half(ws, 1);
+        wait_vmcnt<0>();
+    }
     __syncthreads();
     if (grp == 1) __builtin_amdgcn_s_barrier();   // group 1 runs one phase behind group 0
 
@@ -812,9 +819,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
             epilogue_any(we);
             clear_acc();
         }
-        // B chunk s+1 goes to the buffer of step s-2, whose last readers,
-        // M(s-2) of both groups, ended before this phase.
-        copy_b_half(ws, bn);
+        // Group 0 loads its half of B chunk s+1 (ws) into the buffer of step
+        // s-2, group 1 its half of chunk s+2 (wa) into that of step s-1;
+        // the last readers of each, M(s-2) and M(s-1) of both groups, ended
+        // before this phase.  Each group waits for its half at the end of
+        // its next M phase, so chunk s+1 is whole before U0(s+1) and both
+        // groups read their first B fragments before the U->M barrier.
+        if (grp == 0)
+            copy_b_half(ws, bn);
+        else
+            copy_b_half(wa, bn == 2 ? 0 : bn + 1);
         copy_a32(wa, b);   // staging b held step s, split in U(s-1)
         stores = false;
         if (epi && !reads_c) {
@@ -824,16 +838,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         split_rows(sv, b ^ 1);   // plane buffer b^1 was last read by M(s-1)
         // The first fragments of M(s) are read before the barrier where they
         // are already published: this group's A planes (split in U(s-1),
-        // published by the barrier that ended M(s-1)) and, for group 1 only,
-        // B chunk s (both halves had landed before the barrier that ended
-        // U0(s), which group 0's U(s) precedes).
+        // published by the barrier that ended M(s-1)) and B chunk s (both
+        // halves landed before the barrier that ended the phase before
+        // U0(s)).
         bf16x8_t bfr0[NP], atop0[TM];
         load_afr(b, 0, NP - 1, atop0);
-        if (grp == 1) load_bfr(bm, 0, bfr0);
+        load_bfr(bm, 0, bfr0);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();   // the split's writes drain during M(s)
         __builtin_amdgcn_sched_barrier(0);
-        if (grp == 0) load_bfr(bm, 0, bfr0);
         // ---- M(s) on plane buffer b (split in U(s-1)) and B buffer bm, and
         // the cursor advances for U(s+1).  The MFMAs run in 2 NP groups,
         // (k-half, A plane u) = (0, NP-1) .. (0, 0), (1, NP-1) .. (1, 0); the
@@ -865,18 +878,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         walk_next<SPLIT>(wa, wc);
         bm = bn;
         // Before the next barrier: this thread's split writes of U(s) are
-        // complete (the group reads them in M(s+1)); group 1's half of B
-        // chunk s+1 has landed (group 0 reads it in M(s+1)), its A load of
-        // U(s) and the epilogue's stores, issued after it, may still be in
-        // flight.  Group 0's half landed before U0(s+1)'s own wait, which
-        // precedes the barrier that ends U0(s+1).
+        // complete (the group reads them in M(s+1)); this group's half of B
+        // loaded in U(s) has landed, while its A load of U(s) and the
+        // epilogue's stores, issued after it, may still be in flight.
         wait_lgkmcnt0();
-        if (grp == 1) {
-            if (stores)
-                wait_vmcnt<A_ROUNDS + EPI_STORES>();
-            else
-                wait_vmcnt<A_ROUNDS>();
-        }
+        if (stores)
+            wait_vmcnt<A_ROUNDS + EPI_STORES>();
+        else
+            wait_vmcnt<A_ROUNDS>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
