@@ -873,8 +873,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         }
         epi = wm.kt == (SPLIT ? wm.kt_end : p.nk) - 1;
         we = TilePos{wm.m0, wm.tn, wm.rows, wm.seg};
-        walk_next<SPLIT>(wm, wc);
-        walk_next<SPLIT>(ws, wc);
+        // wm, ws, wa are the same sequence one and two steps apart (past the
+        // end all stay on the last step): one advance, two copies
+        wm = ws;
+        ws = wa;
         walk_next<SPLIT>(wa, wc);
         bm = bn;
         // Before the next barrier: this thread's split writes of U(s) are
