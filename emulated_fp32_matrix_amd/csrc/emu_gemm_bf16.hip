@@ -835,15 +835,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
             stores = epilogue_any(we);
             clear_acc();   // here, not in each epilogue variant: one copy of the clears
         }
-        split_rows(sv, b ^ 1);   // plane buffer b^1 was last read by M(s-1)
         // The first fragments of M(s) are read before the barrier where they
         // are already published: this group's A planes (split in U(s-1),
         // published by the barrier that ended M(s-1)) and B chunk s (both
         // halves landed before the barrier that ended the phase before
-        // U0(s)).
+        // U0(s)).  They are issued before the split, which gives the
+        // staging reads of load_rows longer to land.
         bf16x8_t bfr0[NP], atop0[TM];
         load_afr(b, 0, NP - 1, atop0);
         load_bfr(bm, 0, bfr0);
+        split_rows(sv, b ^ 1);   // plane buffer b^1 was last read by M(s-1)
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();   // the split's writes drain during M(s)
         __builtin_amdgcn_sched_barrier(0);
