@@ -147,22 +147,22 @@ bool valid_op(int op) { return op == EMU_OP_N || op == EMU_OP_T; }
 int64_t max1(int64_t v) { return v > 1 ? v : 1; }
 
 // Cost model of one call on MI355X: predicted device time in microseconds,
-// including the B pre-split and the stream-ordered workspace of the emulated
-// path.  Its form follows the kernels: 128x128 output tiles, K in steps of
+// including the B pre-split of the emulated path (its workspace comes from
+// the per-stream cache).  Its form follows the kernels: 128x128 output tiles, K in steps of
 // 32; the emulated kernel keeps one (tile or K-segment) item per CU (256 at
 // a time), and a k-step costs more once every CU is busy (the clock is then
 // power-limited); the native kernel runs one tile per CU up to 256 tiles and
 // two per CU beyond.  The constants are a least-squares fit (log error) to
 // device times measured with emulated_fp32_matrix_amd/calibrate.py over 67
 // shapes: the MLIP layer stacks, squares 128..8192, skinny shapes and a K
-// sweep.  On those shapes the choice is the faster mode in 65 of 67 cases
-// and within 14 % of it in the other two.
-constexpr double kX9Fixed = 11.62;       // us: pre-split launch, pipeline fill
-constexpr double kX9StepPart = 1.564;    // us per k-step per round while some CUs are idle
-constexpr double kX9StepFull = 2.113;    // us per k-step per round with every CU busy
-constexpr double kF32Fixed = 10.540;
-constexpr double kF32Step1 = 3.045;      // us per k-step, one tile per CU
-constexpr double kF32Step2 = 5.842;      // us per k-step per round of two tiles per CU
+// sweep.  On those shapes the choice is the faster mode in 66 of 67 cases
+// and within 12 % of it in the other.
+constexpr double kX9Fixed = 11.59;       // us: pre-split launch, pipeline fill
+constexpr double kX9StepPart = 1.431;    // us per k-step per round while some CUs are idle
+constexpr double kX9StepFull = 1.984;    // us per k-step per round with every CU busy
+constexpr double kF32Fixed = 10.586;
+constexpr double kF32Step1 = 3.057;      // us per k-step, one tile per CU
+constexpr double kF32Step2 = 5.840;      // us per k-step per round of two tiles per CU
 constexpr double kCUs = 256.0;
 // A split K (S segments of ceil(K/32)/S k-steps each) runs S times as many
 // (segment, tile) items with 1/S of the k-steps each, then a reduction
