@@ -723,9 +723,21 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
                         for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(beta, old[e], out[e]);
                     }
                     if (bias != nullptr) {
-                        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(bias + n0 + col);
+                        // The wave's 8 bias values of register group q sit at a
+                        // wave-uniform address: read them with one scalar load
+                        // (counted by lgkmcnt, so waiting for it never waits for
+                        // the direct loads in flight) and pick this lane's four.
+                        const i32x8_t bv = scalar_load8(bias + n0 + gw * 32 + 8 * q);
+                        const bool upper = (lane >> 5) != 0;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) out[e] = out[e] + bv[e];
+                        for (int e = 0; e < 4; ++e) {
+                            // (opaque copies: otherwise the two selects fold into an
+                            // index into bv and a chain of compares)
+                            int lo = bv[e], hi = bv[4 + e];
+                            asm("" : "+s"(lo));
+                            asm("" : "+s"(hi));
+                            out[e] = out[e] + __int_as_float(upper ? hi : lo);
+                        }
                     }
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, out), rsrc, off, 0, 0);
                 } else {
@@ -795,10 +807,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     // Vector memory operations complete in issue order, so each U phase
     // issues its loads before the epilogue's stores, and the waits below let
     // up to EPI_STORES stores stay in flight into the next phase.  An
-    // epilogue that loads (beta != 0: C; a bias) runs before the loads
-    // instead: the compiler's waits for its own loads would also wait for
-    // the direct loads issued before them.
-    const bool reads_c = !SPLIT && (p.beta != 0.0f || p.bias != nullptr);
+    // epilogue that reads C (beta != 0) runs before the loads instead: the
+    // compiler's waits for its own vector loads would also wait for the
+    // direct loads issued before them.  A bias does not need this: the
+    // vector path reads it through the scalar cache (tiles that cross column
+    // N read it element by element and then wait for the direct loads too,
+    // which costs time only).
+    const bool reads_c = !SPLIT && p.beta != 0.0f;
     bool epi = false;       // U(s) runs the epilogue of step s-1's tile
     bool stores = false;    // the last U phase ended with EPI_STORES stores
     int bm = 0;             // B buffer of step s: s % 3

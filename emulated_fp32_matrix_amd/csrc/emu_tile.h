@@ -124,6 +124,20 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p)
     return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// Eight consecutive 32-bit words at a wave-uniform address, read through the
+// scalar data cache into SGPRs (s_load_dwordx8), for read-only data such as
+// a bias.  The wait is lgkmcnt(0): it never waits for vector memory
+// operations.  Inline assembly, because the compiler may turn uniform loads
+// whose values are then chosen per lane into one vector load per lane.
+__device__ __forceinline__ i32x8_t scalar_load8(const void* p)
+{
+    i32x8_t v;
+    asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
+    return v;
+}
+
 // Direct global->LDS copy of 16 bytes per lane: lane l reads gbase + voff
 // and its bytes land at LDS offset lds_base + 16 l (gbase and lds_base
 // wave-uniform).  Inline assembly keeps the compiler from guarding later LDS
