@@ -34,7 +34,8 @@ STATUS_LAUNCH_FAILED = 3
 
 # C functions declared in include/emu_sgemm.h
 EXPORTS = ("emu_sgemm", "emu_sgemm_bias", "emu_sgemm_ex", "emu_split_bf16x3", "emu_sgemm_select",
-           "emu_sgemm_ksplit", "emu_status_string", "emu_abi_version")
+           "emu_sgemm_ksplit", "emu_presplit_b_bytes", "emu_presplit_b", "emu_sgemm_presplit",
+           "emu_status_string", "emu_abi_version")
 
 
 class EmuError(RuntimeError):
@@ -71,6 +72,13 @@ _lib.emu_sgemm_ex.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, ctyp
 _lib.emu_sgemm_ex.restype = ctypes.c_int
 _lib.emu_sgemm_ksplit.argtypes = [_i64, _i64, _i64, ctypes.POINTER(ctypes.c_int)]
 _lib.emu_sgemm_ksplit.restype = ctypes.c_int
+_lib.emu_presplit_b_bytes.argtypes = [_i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+_lib.emu_presplit_b_bytes.restype = ctypes.c_int
+_lib.emu_presplit_b.argtypes = [ctypes.c_int, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, _vp]
+_lib.emu_presplit_b.restype = ctypes.c_int
+_lib.emu_sgemm_presplit.argtypes = [ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, _vp, _i64, _vp,
+                                    ctypes.c_float, _vp, _i64, _vp, ctypes.c_int, ctypes.c_int, _vp]
+_lib.emu_sgemm_presplit.restype = ctypes.c_int
 _lib.emu_split_bf16x3.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp]
 _lib.emu_split_bf16x3.restype = ctypes.c_int
 _lib.emu_sgemm_select.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64,
@@ -126,6 +134,25 @@ def emu_sgemm_ksplit(M, N, K):
     out = ctypes.c_int(-1)
     st = int(_lib.emu_sgemm_ksplit(int(M), int(N), int(K), ctypes.byref(out)))
     return st, (out.value if st == STATUS_SUCCESS else None)
+
+
+def emu_presplit_b_bytes(N, K, mode):
+    """(status, bytes) of emu_presplit_b_bytes."""
+    out = ctypes.c_size_t(0)
+    st = int(_lib.emu_presplit_b_bytes(int(N), int(K), _mode(mode), ctypes.byref(out)))
+    return st, int(out.value)
+
+
+def emu_presplit_b(transB, N, K, B, ldb, mode, planes, stream) -> int:
+    return int(_lib.emu_presplit_b(int(transB), int(N), int(K), B or None, int(ldb), _mode(mode),
+                                   planes or None, stream or None))
+
+
+def emu_sgemm_presplit(transA, M, N, K, alpha, A, lda, planes, beta, C, ldc, bias, mode, ksplit,
+                       stream) -> int:
+    return int(_lib.emu_sgemm_presplit(int(transA), int(M), int(N), int(K), float(alpha), A or None,
+                                       int(lda), planes or None, float(beta), C or None, int(ldc),
+                                       bias or None, _mode(mode), int(ksplit), stream or None))
 
 
 def emu_split_bf16x3(x, n, hi, mid, lo, stream) -> int:
@@ -220,6 +247,68 @@ def sgemm(a, b, mode="BF16X9", trans_a=False, trans_b=False, alpha=1.0, beta=0.0
                         bias.data_ptr(), mode, _stream_handle(stream))
     if st != STATUS_SUCCESS:
         raise EmuError(st, "emu_sgemm_bias")
+    return c
+
+
+class PresplitB:
+    """op(B) split once into the BF16 planes of ``mode`` (``presplit_b``):
+    ``planes`` is a uint8 CUDA tensor in the library's own layout, valid for
+    GEMMs with this N, K and mode (``sgemm_presplit``)."""
+
+    def __init__(self, planes, N, K, mode):
+        self.planes, self.N, self.K, self.mode = planes, int(N), int(K), mode
+
+
+def presplit_b(b, mode="BF16X9", trans_b=False, stream=None):
+    """Split op(b) (K x N; ``b`` stored as for ``sgemm``) once, for use by
+    ``sgemm_presplit`` in ``mode`` (BF16X9, BF16X6, BF16X3 or BF16X1)."""
+    torch = _torch()
+    _check_matrix(b, "b")
+    K, N = (b.shape[1], b.shape[0]) if trans_b else (b.shape[0], b.shape[1])
+    st, nbytes = emu_presplit_b_bytes(N, K, mode)
+    if st != STATUS_SUCCESS:
+        raise EmuError(st, "emu_presplit_b_bytes")
+    planes = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=b.device)
+    st = emu_presplit_b(OP_T if trans_b else OP_N, N, K, b.data_ptr(), _ld(b), mode,
+                        planes.data_ptr(), _stream_handle(stream))
+    if st != STATUS_SUCCESS:
+        raise EmuError(st, "emu_presplit_b")
+    return PresplitB(planes, N, K, mode)
+
+
+def sgemm_presplit(a, pb, trans_a=False, alpha=1.0, beta=0.0, c=None, bias=None, ksplit=0,
+                   stream=None):
+    """C = alpha * op(a) @ op(B) + beta * c (+ bias) through
+    ``emu_sgemm_presplit``, op(B) given by ``pb = presplit_b(...)``; equal
+    bit for bit to ``sgemm(a, b, pb.mode, ..., ksplit=ksplit)``."""
+    torch = _torch()
+    _check_matrix(a, "a")
+    if not isinstance(pb, PresplitB):
+        raise TypeError("pb must come from presplit_b")
+    M, K = (a.shape[1], a.shape[0]) if trans_a else (a.shape[0], a.shape[1])
+    N = pb.N
+    if K != pb.K:
+        raise ValueError(f"inner dimensions differ: {K} vs {pb.K}")
+    if pb.planes.device != a.device:
+        raise ValueError("a and the planes must be on one device")
+    if c is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs c")
+        c = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    else:
+        _check_matrix(c, "c")
+        if tuple(c.shape) != (M, N):
+            raise ValueError(f"c must be {M}x{N}")
+    if bias is not None and (not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32
+                             or not bias.is_cuda or bias.dim() != 1 or bias.shape[0] != N
+                             or (N > 1 and bias.stride(0) != 1)):
+        raise TypeError(f"bias must be a contiguous float32 CUDA vector of length {N}")
+    st = emu_sgemm_presplit(OP_T if trans_a else OP_N, M, N, K, alpha, a.data_ptr(), _ld(a),
+                            pb.planes.data_ptr(), beta, c.data_ptr(), _ld(c),
+                            bias.data_ptr() if bias is not None else 0, pb.mode, ksplit,
+                            _stream_handle(stream))
+    if st != STATUS_SUCCESS:
+        raise EmuError(st, "emu_sgemm_presplit")
     return c
 
 

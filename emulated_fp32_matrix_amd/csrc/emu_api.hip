@@ -240,10 +240,12 @@ emu_status_t from_hip(hipError_t e)
 
 namespace {
 
+// planes: op(B) pre-split by emu_presplit_b (then B, ldb and transB are not
+// used and mode must be an emulated one), or null.
 emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
                         float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
                         float beta, float* C, int64_t ldc, const float* bias, emu_mode_t mode,
-                        int ksplit, void* stream)
+                        int ksplit, void* stream, const void* planes = nullptr)
 {
     // ---- validation: no HIP call before this block has passed ----
     if (!valid_op(transA) || !valid_op(transB)) return EMU_STATUS_INVALID_VALUE;
@@ -253,11 +255,13 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     if (ksplit > 1 && (K == 0 || ((K + 31) / 32) % ksplit != 0)) return EMU_STATUS_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return EMU_STATUS_INVALID_VALUE;
     if (lda < (transA == EMU_OP_N ? max1(K) : max1(M))) return EMU_STATUS_INVALID_VALUE;
-    if (ldb < (transB == EMU_OP_N ? max1(N) : max1(K))) return EMU_STATUS_INVALID_VALUE;
+    if (planes == nullptr && ldb < (transB == EMU_OP_N ? max1(N) : max1(K))) return EMU_STATUS_INVALID_VALUE;
     if (ldc < max1(N)) return EMU_STATUS_INVALID_VALUE;
     const bool has_c = M > 0 && N > 0;
     if (has_c && C == nullptr) return EMU_STATUS_INVALID_VALUE;
-    if (has_c && K > 0 && (A == nullptr || B == nullptr)) return EMU_STATUS_INVALID_VALUE;
+    if (has_c && K > 0 && (A == nullptr || (B == nullptr && planes == nullptr)))
+        return EMU_STATUS_INVALID_VALUE;
+    if (planes != nullptr && ((uintptr_t)planes & 15u) != 0) return EMU_STATUS_INVALID_VALUE;
     if (!has_c) return EMU_STATUS_SUCCESS;
 
     emu::DeviceInfo dev;
@@ -283,6 +287,7 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     g.C = C;
     g.ldc = ldc;
     g.bias = bias;
+    g.Bplanes = static_cast<const uint16_t*>(planes);
     if (mode == EMU_MODE_NATIVE_F32) return from_hip(emu::launch_gemm_native_f32(g, dev, s));
     const bool fused = emu::fused_a_path(g);
     if (ksplit > 1 && !fused) return EMU_STATUS_NOT_SUPPORTED;
@@ -299,9 +304,22 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     default: return EMU_STATUS_INTERNAL;
     }
     void* ws = nullptr;
-    if (stream_workspace(dev, s, emu::gemm_bf16_workspace_bytes(g, nbands, ksplit), &ws) != hipSuccess)
+    const size_t ws_bytes = emu::gemm_bf16_workspace_bytes(g, nbands, ksplit);
+    if (ws_bytes > 0 && stream_workspace(dev, s, ws_bytes, &ws) != hipSuccess)
         return EMU_STATUS_ALLOC_FAILED;
     return from_hip(emu::launch_gemm_bf16(g, nbands, ksplit, dev, ws, s));
+}
+
+// Bands of an emulated mode (0 for NATIVE_F32 and AUTO).
+int mode_bands(emu_mode_t mode)
+{
+    switch (mode) {
+    case EMU_MODE_BF16X9: return 5;
+    case EMU_MODE_BF16X6: return 3;
+    case EMU_MODE_BF16X3: return 2;
+    case EMU_MODE_BF16X1: return 1;
+    default: return 0;
+    }
 }
 
 }  // namespace
@@ -321,7 +339,7 @@ const char* emu_status_string(emu_status_t status)
     }
 }
 
-int emu_abi_version(void) { return 103; }
+int emu_abi_version(void) { return 104; }
 
 emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
                               emu_mode_t* chosen)
@@ -356,6 +374,37 @@ emu_status_t emu_sgemm_ex(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N
 {
     return sgemm_impl(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, mode,
                       ksplit, stream);
+}
+
+emu_status_t emu_presplit_b_bytes(int64_t N, int64_t K, emu_mode_t mode, size_t* bytes)
+{
+    if (N < 0 || K < 0 || bytes == nullptr || mode_bands(mode) == 0) return EMU_STATUS_INVALID_VALUE;
+    *bytes = N == 0 || K == 0 ? 0 : emu::gemm_bf16_planes_bytes(N, K, mode_bands(mode));
+    return EMU_STATUS_SUCCESS;
+}
+
+emu_status_t emu_presplit_b(emu_op_t transB, int64_t N, int64_t K, const float* B, int64_t ldb,
+                            emu_mode_t mode, void* planes, void* stream)
+{
+    if (!valid_op(transB) || N < 0 || K < 0 || mode_bands(mode) == 0) return EMU_STATUS_INVALID_VALUE;
+    if (ldb < (transB == EMU_OP_N ? max1(N) : max1(K))) return EMU_STATUS_INVALID_VALUE;
+    if (N == 0 || K == 0) return EMU_STATUS_SUCCESS;
+    if (B == nullptr || planes == nullptr || ((uintptr_t)planes & 15u) != 0) return EMU_STATUS_INVALID_VALUE;
+    emu::DeviceInfo dev;
+    if (!current_device(dev)) return EMU_STATUS_NOT_SUPPORTED;
+    return from_hip(emu::launch_presplit_b(B, ldb, transB == EMU_OP_T, N, K, mode_bands(mode),
+                                           static_cast<uint16_t*>(planes), static_cast<hipStream_t>(stream)));
+}
+
+emu_status_t emu_sgemm_presplit(emu_op_t transA, int64_t M, int64_t N, int64_t K, float alpha,
+                                const float* A, int64_t lda, const void* planes, float beta, float* C,
+                                int64_t ldc, const float* bias, emu_mode_t mode, int ksplit, void* stream)
+{
+    if (mode_bands(mode) == 0) return EMU_STATUS_INVALID_VALUE;
+    if (M > 0 && N > 0 && K > 0 && planes == nullptr) return EMU_STATUS_INVALID_VALUE;
+    // (B and ldb are not read; ldb = max(1, N) passes the op(B) check)
+    return sgemm_impl(transA, EMU_OP_N, M, N, K, alpha, A, lda, nullptr, max1(N), beta, C, ldc, bias,
+                      mode, ksplit, stream, planes);
 }
 
 emu_status_t emu_sgemm_ksplit(int64_t M, int64_t N, int64_t K, int* ksplit)

@@ -1038,7 +1038,7 @@ WsLayout ws_layout(const GemmArgs& g, int nbands, int ksplit)
     const bool fused = fused_a_path(g);
     WsLayout w;
     w.b = 0;
-    w.a = round256((size_t)(tiles_n * nk * chunk_elems(np)) * sizeof(uint16_t));
+    w.a = g.Bplanes != nullptr ? 0 : round256((size_t)(tiles_n * nk * chunk_elems(np)) * sizeof(uint16_t));
     w.c = w.a + (fused ? 0 : round256((size_t)(tiles_m * nk * chunk_elems(np)) * sizeof(uint16_t)));
     w.total = w.c + (ksplit > 1 ? round256((size_t)ksplit * (size_t)g.M * (size_t)g.N * sizeof(float)) : 0);
     return w;
@@ -1049,6 +1049,26 @@ WsLayout ws_layout(const GemmArgs& g, int nbands, int ksplit)
 size_t gemm_bf16_workspace_bytes(const GemmArgs& g, int nbands, int ksplit)
 {
     return ws_layout(g, nbands, ksplit).total;
+}
+
+size_t gemm_bf16_planes_bytes(int64_t N, int64_t K, int nbands)
+{
+    const int np = nbands >= 3 ? 3 : nbands;
+    const int64_t tiles_n = (N + TILE - 1) / TILE;
+    const int64_t nk = (K + BK - 1) / BK;
+    return (size_t)(tiles_n * nk * chunk_elems(np)) * sizeof(uint16_t);
+}
+
+hipError_t launch_presplit_b(const float* B, int64_t ldb, bool trans_b, int64_t N, int64_t K,
+                             int nbands, uint16_t* planes, hipStream_t stream)
+{
+    if (nbands != 5 && nbands != 3 && nbands != 2 && nbands != 1) return hipErrorInvalidValue;
+    const int64_t tiles_n = (N + TILE - 1) / TILE;
+    const int64_t nk = (K + BK - 1) / BK;
+    const int64_t lim = (int64_t)1 << 31;
+    if (tiles_n * nk >= lim || ((uintptr_t)planes & 15u) != 0) return hipErrorInvalidValue;
+    return launch_presplit(nbands >= 3 ? 3 : nbands, B, ldb, trans_b, N, K, (int)tiles_n, (int)nk,
+                           planes, stream);
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const DeviceInfo& dev,
@@ -1063,8 +1083,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const Dev
         tiles_m * nk >= lim)
         return hipErrorInvalidValue;
     const bool fused = fused_a_path(g);
+    const WsLayout lay = ws_layout(g, nbands, ksplit);
     if (ksplit < 1 || nk % ksplit != 0 || (ksplit > 1 && !fused) ||
-        tiles_m * tiles_n * ksplit >= lim || workspace == nullptr)
+        tiles_m * tiles_n * ksplit >= lim || (workspace == nullptr && lay.total > 0) ||
+        ((uintptr_t)g.Bplanes & 15u) != 0)
         return hipErrorInvalidValue;
 
     Params p{};
@@ -1094,13 +1116,16 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const Dev
     p.vec_ws = ((g.N & 3) == 0 && (int64_t)TILE * g.N * 4 < ((int64_t)1 << 31)) ? 1 : 0;
 
     const int np = nbands >= 3 ? 3 : nbands;
-    const WsLayout lay = ws_layout(g, nbands, ksplit);
     char* ws = static_cast<char*>(workspace);
-    uint16_t* Wb = reinterpret_cast<uint16_t*>(ws + lay.b);
+    // (the kernels only read the B planes)
+    uint16_t* Wb = g.Bplanes != nullptr ? const_cast<uint16_t*>(g.Bplanes)
+                                        : reinterpret_cast<uint16_t*>(ws + lay.b);
     uint16_t* Wa = fused ? nullptr : reinterpret_cast<uint16_t*>(ws + lay.a);
     p.wsC = ksplit > 1 ? reinterpret_cast<float*>(ws + lay.c) : nullptr;
 
-    hipError_t e = launch_presplit(np, g.B, g.ldb, g.trans_b, g.N, g.K, (int)tiles_n, (int)nk, Wb, stream);
+    hipError_t e = hipSuccess;
+    if (g.Bplanes == nullptr)
+        e = launch_presplit(np, g.B, g.ldb, g.trans_b, g.N, g.K, (int)tiles_n, (int)nk, Wb, stream);
     if (e == hipSuccess && !fused)
         e = launch_presplit(np, g.A, g.lda, !g.trans_a, g.M, g.K, (int)tiles_m, (int)nk, Wa, stream);
     if (e == hipSuccess) {

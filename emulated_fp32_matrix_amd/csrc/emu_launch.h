@@ -19,6 +19,9 @@ struct GemmArgs {
     float* C;
     int64_t ldc;
     const float* bias;   // length N or null
+    // op(B) already split by launch_presplit_b (same N, K and plane count),
+    // or null: the call splits op(B) into its workspace
+    const uint16_t* Bplanes = nullptr;
 };
 
 struct DeviceInfo {
@@ -42,6 +45,13 @@ size_t gemm_bf16_workspace_bytes(const GemmArgs& g, int nbands, int ksplit);
 hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const DeviceInfo& dev,
                             void* workspace, hipStream_t stream);
 hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, hipStream_t stream);
+// The BF16 planes of op(B) (K x N; element (k, n) is B[n*ldb + k] when
+// trans_b, else B[k*ldb + n]) in the layout the emulated kernels read:
+// their size in bytes, and the split into `planes` (16-byte aligned) for
+// nbands 5, 3, 2 or 1.
+size_t gemm_bf16_planes_bytes(int64_t N, int64_t K, int nbands);
+hipError_t launch_presplit_b(const float* B, int64_t ldb, bool trans_b, int64_t N, int64_t K,
+                             int nbands, uint16_t* planes, hipStream_t stream);
 // C = beta * C + bias over M x N (C not read when beta == 0; bias may be null).
 hipError_t launch_scale_c(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
                           const float* bias, hipStream_t stream);

@@ -17,6 +17,13 @@ in_features]):
 
 The mode ("AUTO" = the performant policy, "BF16X9" = eager, "BF16X6",
 "BF16X3", "NATIVE_F32") applies to both library GEMMs.
+
+With cache_weights=True the layer keeps the BF16 planes of W (for the
+forward GEMM) and of W^T (for the input gradient), made by emu_presplit_b,
+and runs the emulated GEMMs through emu_sgemm_presplit, which then skips
+splitting the weights on every call; results are bit-identical.  The cache
+is keyed by the weight's storage, shape, version counter and the mode, so an
+optimizer step or load_state_dict (in-place updates) invalidates it.
 """
 from __future__ import annotations
 
@@ -24,7 +31,44 @@ import math
 
 import torch
 
-from . import sgemm
+from . import presplit_b, select_ksplit, select_mode, sgemm, sgemm_presplit
+
+_EMULATED = ("BF16X9", "BF16X6", "BF16X3", "BF16X1")
+
+
+class _PlanesCache:
+    """Planes of one op(B) of a weight, rebuilt when the weight changes."""
+
+    def __init__(self, trans_b):
+        self.trans_b = trans_b
+        self.key = None
+        self.planes = None
+
+    def get(self, w, mode):
+        key = (w.data_ptr(), tuple(w.shape), w._version, mode, w.device)
+        if key != self.key:
+            self.planes = presplit_b(w, mode=mode, trans_b=self.trans_b)
+            self.key = key
+        return self.planes
+
+
+def _gemm(a, w, trans_b, mode, bias, cache):
+    """a @ op(w) (+ bias) in `mode`; with a cache and an emulated mode (the
+    one AUTO would run, when mode is AUTO) through the weight's planes, with
+    the K split the library would choose itself, so the result is the same
+    bit for bit."""
+    if cache is None:
+        return sgemm(a, w, mode=mode, trans_b=trans_b, bias=bias)
+    M, K = a.shape
+    N = w.shape[0] if trans_b else w.shape[1]
+    run = select_mode(M, N, K) if mode == "AUTO" else mode
+    if run not in _EMULATED:
+        return sgemm(a, w, mode=run, trans_b=trans_b, bias=bias)
+    # the library splits K only under AUTO and only where A is split inside
+    # the GEMM (k-contiguous rows, 16-byte aligned, K a multiple of 4)
+    fused = a.data_ptr() % 16 == 0 and K % 4 == 0 and a.stride(0) % 4 == 0
+    ksplit = select_ksplit(M, N, K) if mode == "AUTO" and fused else 1
+    return sgemm_presplit(a, cache.get(w, run), bias=bias, ksplit=ksplit)
 
 
 def _as_rows(t, width):
@@ -34,16 +78,17 @@ def _as_rows(t, width):
 
 class _EmuLinearFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, weight, bias, mode):
+    def forward(ctx, x, weight, bias, mode, caches):
         if x.dtype != torch.float32 or weight.dtype != torch.float32:
             raise TypeError("EmuLinear computes in float32")
         out_f, in_f = weight.shape
         x2 = _as_rows(x, in_f)
         w = weight if weight.is_contiguous() else weight.contiguous()
-        y = sgemm(x2, w, mode=mode, trans_b=True, bias=bias)
+        y = _gemm(x2, w, True, mode, bias, caches[0] if caches and w is weight else None)
         ctx.save_for_backward(x2, w)
         ctx.has_bias = bias is not None
         ctx.mode = mode
+        ctx.caches = caches if w is weight else None
         ctx.x_shape = x.shape
         return y.reshape(*x.shape[:-1], out_f)
 
@@ -54,7 +99,8 @@ class _EmuLinearFunction(torch.autograd.Function):
         gy2 = _as_rows(gy, out_f)
         gx = gw = gb = None
         if ctx.needs_input_grad[0]:
-            gx = sgemm(gy2, w, mode=ctx.mode).reshape(ctx.x_shape)
+            gx = _gemm(gy2, w, False, ctx.mode, None,
+                       ctx.caches[1] if ctx.caches else None).reshape(ctx.x_shape)
         if ctx.needs_input_grad[1]:
             prev = torch.backends.cuda.matmul.allow_tf32
             torch.backends.cuda.matmul.allow_tf32 = False
@@ -64,7 +110,7 @@ class _EmuLinearFunction(torch.autograd.Function):
                 torch.backends.cuda.matmul.allow_tf32 = prev
         if ctx.has_bias and ctx.needs_input_grad[2]:
             gb = gy2.sum(dim=0)
-        return gx, gw, gb, None
+        return gx, gw, gb, None, None
 
 
 class EmuLinear(torch.nn.Module):
@@ -74,11 +120,14 @@ class EmuLinear(torch.nn.Module):
     either way; :meth:`from_linear` wraps an existing layer's parameters.
     """
 
-    def __init__(self, in_features, out_features, bias=True, mode="AUTO", device=None):
+    def __init__(self, in_features, out_features, bias=True, mode="AUTO", device=None,
+                 cache_weights=False):
         super().__init__()
         self.in_features = in_features
         self.out_features = out_features
         self.mode = mode
+        # planes of W^T (forward) and W (input gradient), or None
+        self._caches = (_PlanesCache(True), _PlanesCache(False)) if cache_weights else None
         self.weight = torch.nn.Parameter(torch.empty(out_features, in_features, device=device,
                                                      dtype=torch.float32))
         if bias:
@@ -96,9 +145,9 @@ class EmuLinear(torch.nn.Module):
             torch.nn.init.uniform_(self.bias, -bound, bound)
 
     @classmethod
-    def from_linear(cls, linear, mode="AUTO"):
+    def from_linear(cls, linear, mode="AUTO", cache_weights=False):
         m = cls(linear.in_features, linear.out_features, bias=linear.bias is not None, mode=mode,
-                device=linear.weight.device)
+                device=linear.weight.device, cache_weights=cache_weights)
         with torch.no_grad():
             m.weight.copy_(linear.weight)
             if linear.bias is not None:
@@ -106,8 +155,9 @@ class EmuLinear(torch.nn.Module):
         return m
 
     def forward(self, x):
-        return _EmuLinearFunction.apply(x, self.weight, self.bias, self.mode)
+        return _EmuLinearFunction.apply(x, self.weight, self.bias, self.mode, self._caches)
 
     def extra_repr(self):
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
-                f"bias={self.bias is not None}, mode={self.mode}")
+                f"bias={self.bias is not None}, mode={self.mode}, "
+                f"cache_weights={self._caches is not None}")

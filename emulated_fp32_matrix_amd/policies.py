@@ -4,7 +4,10 @@ The policies of "Unlocking Tensor Core Performance for Machine Learning
 Interatomic Potentials" (section "BF16x9 on NVIDIA Blackwell GPUs"):
 "performant" uses the emulation only where it is predicted to be faster
 (EMU_MODE_AUTO), "eager" uses it wherever it applies (EMU_MODE_BF16X9);
-"native" never does (EMU_MODE_NATIVE_F32).  BF16X6 is timed beside them.
+"native" never does (EMU_MODE_NATIVE_F32).  BF16X6 is timed beside them, and
+"performant_cached": AUTO's choices with every emulated GEMM's weights split
+once beforehand (emu_presplit_b) and used by emu_sgemm_presplit, as a fixed
+model in inference or molecular dynamics allows.
 
 Per stack and policy it reports the step time two ways:
   wall   - HIP events around the 8 calls issued back to back, what a caller
@@ -29,7 +32,8 @@ import os
 import statistics
 import sys
 
-POLICIES = {"performant": "AUTO", "eager": "BF16X9", "native": "NATIVE_F32", "bf16x6": "BF16X6"}
+POLICIES = {"performant": "AUTO", "eager": "BF16X9", "native": "NATIVE_F32", "bf16x6": "BF16X6",
+            "performant_cached": "AUTO+planes"}
 
 
 def _synth():
@@ -58,11 +62,20 @@ def time_stack(stack, reps=5):
     flops = sum(g.flops for g in gemms)
     choice = {g.name: emu.select_mode(g.M, g.N, g.K, g.trans_a, g.trans_b) for g in gemms}
 
+    splits = {g.name: emu.select_ksplit(g.M, g.N, g.K) for g in gemms}
+    # "AUTO+planes": AUTO's choices with the weights split once beforehand
+    # (emu_presplit_b, outside the timed region) and emu_sgemm_presplit
+    planes = {g.name: emu.presplit_b(b, mode="BF16X9", trans_b=g.trans_b)
+              for g, a, b, c in tensors if choice[g.name] == "BF16X9"}
+
     def step(mode):
         for g, a, b, c in tensors:
-            emu.sgemm(a, b, mode=mode, trans_a=g.trans_a, trans_b=g.trans_b, c=c)
+            if mode == "AUTO+planes" and g.name in planes:
+                emu.sgemm_presplit(a, planes[g.name], trans_a=g.trans_a, c=c, ksplit=splits[g.name])
+            else:
+                emu.sgemm(a, b, mode="AUTO" if mode == "AUTO+planes" else mode, trans_a=g.trans_a,
+                          trans_b=g.trans_b, c=c)
 
-    splits = {g.name: emu.select_ksplit(g.M, g.N, g.K) for g in gemms}
     out = {"stack": stack, "name": synth.CONFIG_NAMES[stack], "gflop": flops / 1e9,
            "auto_choice": choice, "auto_ksplit": splits, "policies": {}}
     for pol, mode in POLICIES.items():

@@ -51,6 +51,7 @@
 #ifndef EMU_SGEMM_H
 #define EMU_SGEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -193,6 +194,55 @@ emu_status_t emu_sgemm_ex(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N
 emu_status_t emu_sgemm_ksplit(int64_t M, int64_t N, int64_t K, int* ksplit);
 
 /*
+ * Weights split once, used by many GEMMs.  Every emulated call splits op(B)
+ * into BF16 planes before its GEMM (the split of "Unlocking Tensor Core
+ * Performance for Machine Learning Interatomic Potentials", section "How
+ * Tensor Core FP32 bridges the hardware gap", Figure 1).  When op(B) is a
+ * layer's weight matrix that does not change between calls, as in inference
+ * or molecular dynamics with a fixed model, the caller can split it once
+ * with emu_presplit_b and pass the planes to emu_sgemm_presplit, which then
+ * skips that step (a separate launch: a sizeable part of a small GEMM's
+ * time).  The result equals emu_sgemm_ex's with the same op(B), mode and
+ * ksplit, bit for bit.
+ *
+ * emu_presplit_b_bytes: device bytes the planes of a K x N op(B) take in
+ * `mode` (EMU_MODE_BF16X9, X6, X3 or X1; the planes depend on the mode: 3
+ * planes for X9 and X6, 2 for X3, 1 for X1); 0 when N or K is 0.
+ * Errors: EMU_STATUS_INVALID_VALUE for negative dimensions, a NULL `bytes`
+ * or a mode other than those four.
+ */
+emu_status_t emu_presplit_b_bytes(int64_t N, int64_t K, emu_mode_t mode, size_t* bytes);
+
+/*
+ * emu_presplit_b: write the planes of op(B) (K x N; B stored as for
+ * emu_sgemm with transB and ldb) to `planes`: caller-owned device memory of
+ * at least emu_presplit_b_bytes(N, K, mode) bytes, 16-byte aligned.  The
+ * layout is the library's own (opaque; it may change with the ABI version).
+ * Asynchronous on `stream`; `planes` is ready for calls ordered after it.
+ * Errors: EMU_STATUS_INVALID_VALUE for a bad enum, a mode other than the
+ * four emulated ones, negative dimensions, ldb too small, or (N, K > 0) a
+ * NULL B or planes or planes not 16-byte aligned; NOT_SUPPORTED /
+ * LAUNCH_FAILED as for emu_sgemm.
+ */
+emu_status_t emu_presplit_b(emu_op_t transB, int64_t N, int64_t K, const float* B, int64_t ldb,
+                            emu_mode_t mode, void* planes, void* stream);
+
+/*
+ * emu_sgemm_presplit: as emu_sgemm_ex, with op(B) given by planes that
+ * emu_presplit_b wrote for the same N, K and mode (a mismatch is not
+ * detected: the caller keeps them together).  `mode` must be one of the
+ * four emulated modes; ksplit 0 or 1 is no split, S > 1 as in emu_sgemm_ex
+ * (emu_sgemm_ksplit gives the split EMU_MODE_AUTO would use).
+ * Errors: as emu_sgemm_ex (without the op(B) checks); also
+ * EMU_STATUS_INVALID_VALUE for NATIVE_F32 or AUTO, or (M, N, K > 0) NULL or
+ * non-16-byte-aligned planes.
+ */
+emu_status_t emu_sgemm_presplit(emu_op_t transA, int64_t M, int64_t N, int64_t K, float alpha,
+                                const float* A, int64_t lda, const void* planes, float beta, float* C,
+                                int64_t ldc, const float* bias, emu_mode_t mode, int ksplit,
+                                void* stream);
+
+/*
  * The exact three-piece split on its own (Figure 1): for i < n,
  *   hi[i], mid[i], lo[i] = BF16 bit patterns of hi, mid', lo' of x[i]
  * with x[i] == hi + 2^-8 mid' + 2^-16 lo' exactly for every finite x[i].
@@ -221,9 +271,10 @@ emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64
  * codes give "EMU_STATUS_UNKNOWN".  Never NULL. */
 const char* emu_status_string(emu_status_t status);
 
-/* ABI version of this header (major * 100 + minor): 103 (1.1 added
+/* ABI version of this header (major * 100 + minor): 104 (1.1 added
  * emu_sgemm_bias, 1.2 EMU_MODE_BF16X1, 1.3 emu_sgemm_ex and
- * emu_sgemm_ksplit). */
+ * emu_sgemm_ksplit, 1.4 emu_presplit_b_bytes, emu_presplit_b and
+ * emu_sgemm_presplit). */
 int emu_abi_version(void);
 
 #ifdef __cplusplus

@@ -45,7 +45,7 @@ def test_status_strings_and_version():
     assert emu.emu_status_string(2) == "EMU_STATUS_NOT_SUPPORTED"
     assert emu.emu_status_string(3) == "EMU_STATUS_LAUNCH_FAILED"
     assert emu.emu_status_string(99) == "EMU_STATUS_UNKNOWN"
-    assert emu.emu_abi_version() == 103
+    assert emu.emu_abi_version() == 104
 
 
 FAKE = 0x1000  # never dereferenced: validation fails (or returns) before any HIP call
@@ -106,6 +106,59 @@ def test_split_entry_point_invalid_arguments_rejected(args):
                 beta=0.0, C=FAKE, ldc=6, bias=0, mode=1, ksplit=2, stream=0)
     call.update(args)
     assert emu.emu_sgemm_ex(**call) == emu.STATUS_INVALID_VALUE
+
+
+def test_presplit_sizes():
+    """Planes of a K x N op(B): ceil(N/128) tiles x ceil(K/32) k-steps x
+    planes x 128 x 32 BF16 values; 0 when N or K is 0."""
+    for mode, planes in (("BF16X9", 3), ("BF16X6", 3), ("BF16X3", 2), ("BF16X1", 1)):
+        st, n = emu.emu_presplit_b_bytes(256, 256, mode)
+        assert st == emu.STATUS_SUCCESS and n == 2 * 8 * planes * 128 * 32 * 2, (mode, n)
+        st, n = emu.emu_presplit_b_bytes(129, 33, mode)   # ragged: 2 tiles, 2 k-steps
+        assert st == emu.STATUS_SUCCESS and n == 2 * 2 * planes * 128 * 32 * 2, (mode, n)
+        assert emu.emu_presplit_b_bytes(0, 64, mode) == (emu.STATUS_SUCCESS, 0)
+        assert emu.emu_presplit_b_bytes(64, 0, mode) == (emu.STATUS_SUCCESS, 0)
+
+
+@pytest.mark.parametrize("N,K,mode", [(-1, 4, "BF16X9"), (4, -1, "BF16X9"), (4, 4, "NATIVE_F32"),
+                                      (4, 4, "AUTO")])
+def test_presplit_bytes_invalid(N, K, mode):
+    assert emu.emu_presplit_b_bytes(N, K, mode)[0] == emu.STATUS_INVALID_VALUE
+
+
+def test_presplit_bytes_null_output():
+    assert emu._lib.emu_presplit_b_bytes(4, 4, 1, None) == emu.STATUS_INVALID_VALUE
+
+
+@pytest.mark.parametrize("args", [
+    dict(transB=2), dict(mode="NATIVE_F32"), dict(mode="AUTO"), dict(N=-1), dict(K=-2),
+    dict(ldb=5),                    # NN: ldb >= N = 6
+    dict(transB=1, ldb=63),         # NT: ldb >= K = 64
+    dict(B=0), dict(planes=0), dict(planes=FAKE + 4),   # planes must be 16-byte aligned
+])
+def test_presplit_invalid_arguments_rejected(args):
+    call = dict(transB=0, N=6, K=64, B=FAKE, ldb=6, mode="BF16X9", planes=FAKE, stream=0)
+    call.update(args)
+    assert emu.emu_presplit_b(**call) == emu.STATUS_INVALID_VALUE
+
+
+@pytest.mark.parametrize("args", [
+    dict(mode="NATIVE_F32"), dict(mode="AUTO"), dict(planes=0), dict(planes=FAKE + 8),
+    dict(transA=2), dict(M=-1), dict(lda=63), dict(C=0), dict(A=0), dict(ldc=5),
+    dict(ksplit=-1), dict(ksplit=3),   # K = 64: 2 k-steps, 3 does not divide them
+])
+def test_sgemm_presplit_invalid_arguments_rejected(args):
+    call = dict(transA=0, M=10, N=6, K=64, alpha=1.0, A=FAKE, lda=64, planes=FAKE, beta=0.0, C=FAKE,
+                ldc=6, bias=0, mode="BF16X9", ksplit=0, stream=0)
+    call.update(args)
+    assert emu.emu_sgemm_presplit(**call) == emu.STATUS_INVALID_VALUE
+
+
+def test_presplit_empty_shapes_return_before_touching_the_device():
+    assert emu.emu_presplit_b(0, 0, 64, 0, 1, "BF16X9", 0, 0) == emu.STATUS_SUCCESS
+    assert emu.emu_presplit_b(0, 6, 0, 0, 6, "BF16X9", 0, 0) == emu.STATUS_SUCCESS
+    assert emu.emu_sgemm_presplit(0, 0, 6, 64, 1.0, 0, 64, 0, 0.0, 0, 6, 0, "BF16X9", 0, 0) == \
+        emu.STATUS_SUCCESS
 
 
 def test_ksplit_choice_is_pure_and_follows_the_cost_model():

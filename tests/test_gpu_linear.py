@@ -189,3 +189,46 @@ def test_emulinear_matches_nn_linear_and_state_dict():
     layer.zero_grad()
     layer(x).sum().backward()
     assert layer.weight.grad is not None and layer.bias.grad is not None
+
+
+@pytest.mark.parametrize("mode", ["AUTO", "BF16X9", "BF16X3", "NATIVE_F32"])
+def test_emulinear_cached_weights_bitwise(mode):
+    """cache_weights=True (weights split once, emu_sgemm_presplit) gives the
+    uncached layer's forward output and input gradient bit for bit, for row
+    counts where AUTO splits K (6,144) and where it does not; an optimizer
+    step invalidates the cache; a second forward with unchanged weights
+    reuses it."""
+    import torch
+
+    from emulated_fp32_matrix_amd.linear import EmuLinear
+
+    torch.manual_seed(5)
+    ref = EmuLinear(256, 768, mode=mode).cuda()
+    cached = EmuLinear(256, 768, mode=mode, cache_weights=True).cuda()
+    cached.load_state_dict(ref.state_dict())
+    opt = torch.optim.SGD(cached.parameters(), lr=0.1)
+    opt_ref = torch.optim.SGD(ref.parameters(), lr=0.1)
+    for step, rows in enumerate((6144, 300, 6144)):
+        x = torch.randn(rows, 256, device="cuda", requires_grad=True)
+        xr = x.detach().clone().requires_grad_(True)
+        y, yr = cached(x), ref(xr)
+        g = torch.randn_like(y)
+        y.backward(g)
+        yr.backward(g)
+        torch.cuda.synchronize()
+        assert torch.equal(y.detach().view(torch.int32), yr.detach().view(torch.int32)), (mode, step)
+        assert torch.equal(x.grad.view(torch.int32), xr.grad.view(torch.int32)), (mode, step)
+        say(f"{mode} step {step} ({rows} rows): cached forward and input gradient bitwise equal")
+        opt.step()
+        opt_ref.step()
+        opt.zero_grad()
+        opt_ref.zero_grad()
+    if mode != "NATIVE_F32":
+        with torch.no_grad():
+            cached(torch.randn(64, 256, device="cuda"))
+            first = cached._caches[0].planes
+            cached(torch.randn(128, 256, device="cuda"))
+            assert cached._caches[0].planes is first   # unchanged weights: the same planes
+            cached.weight.add_(1.0)
+            cached(torch.randn(64, 256, device="cuda"))
+            assert cached._caches[0].planes is not first   # in-place update: split again
