@@ -66,7 +66,7 @@ KERNEL_SOURCES = ("emulated_fp32_matrix_amd/csrc/emu_gemm_bf16.hip",
 # WRITE_SIZE) scaled by the same counters' reading for a 1 GiB device copy.
 # Keyed by the SHA-256 of KERNEL_SOURCES: a changed kernel reports null.
 TRAFFIC_BY_SOURCE = {
-    "704ea29d05ad0ddc625e78c43bdc23f527ac727f1d5e7b0f3f6e1ef2656d420b": 1854942587,
+    "ec09c45601f0d158806d74a24a5ba7baf4f7d9b384b2a1bb706ebcd26d53311f": 1858746995,
 }
 
 
