@@ -31,7 +31,8 @@ if _ROOT not in sys.path:
 BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, 256 CUs x 4096 flop/clk x 2.4 GHz
 F32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 HBM_PEAK_GBS = 8000.0
-PRODUCTS = {"BF16X9": 9, "BF16X6": 6, "BF16X3": 3, "NATIVE_F32": 1}
+PRODUCTS = {"BF16X9": 9, "BF16X6": 6, "BF16X3": 3, "BF16X1": 1, "NATIVE_F32": 1}
+BANDS = {"BF16X9": 5, "BF16X6": 3, "BF16X3": 2, "BF16X1": 1}
 WORKLOAD = 3
 
 
@@ -44,7 +45,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--mode", default="BF16X9")
+    ap.add_argument("--mode", default="BF16X9", type=str.upper,
+                    choices=["BF16X9", "BF16X6", "BF16X3", "BF16X1", "NATIVE_F32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the NATIVE_F32 and torch-fp32 context timings")
@@ -218,15 +220,15 @@ def main():
     P = PRODUCTS[mode]
     n_launch = len(gemms)
     avg_us = float(per.sum()) / n_launch * 1e3
-    peak = BF16_PEAK_TFLOPS if P > 1 else F32_PEAK_TFLOPS
+    peak = BF16_PEAK_TFLOPS if mode in BANDS else F32_PEAK_TFLOPS
     achieved = P * float(flops.sum()) / n_launch / (avg_us * 1e-6) / 1e12
     traffic = None
     if mode == "BF16X9":
         traffic = TRAFFIC_BY_SOURCE.get(kernel_source_hash())
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel": ("gemm_bf16_pp_kernel<%d, false>" % {9: 5, 6: 3, 3: 2}[P])
-                if P > 1 else "gemm_f32_kernel",
+                "kernel": ("gemm_bf16_pp_kernel<%d, false>" % BANDS[mode])
+                if mode in BANDS else "gemm_f32_pp_kernel",
                 "avg_launch_us": round(avg_us, 2),
                 "algorithmic_flop_per_launch": round(P * float(flops.sum()) / n_launch)}
 

@@ -288,7 +288,13 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     g.ldc = ldc;
     g.bias = bias;
     g.Bplanes = static_cast<const uint16_t*>(planes);
-    if (mode == EMU_MODE_NATIVE_F32) return from_hip(emu::launch_gemm_native_f32(g, dev, s));
+    if (mode == EMU_MODE_NATIVE_F32) {
+        void* ws = nullptr;
+        const size_t ws_bytes = emu::gemm_native_f32_workspace_bytes(g);
+        if (ws_bytes > 0 && stream_workspace(dev, s, ws_bytes, &ws) != hipSuccess)
+            return EMU_STATUS_ALLOC_FAILED;
+        return from_hip(emu::launch_gemm_native_f32(g, dev, ws, s));
+    }
     const bool fused = emu::fused_a_path(g);
     if (ksplit > 1 && !fused) return EMU_STATUS_NOT_SUPPORTED;
     // ksplit 0: the performant policy (AUTO) may split where its cost model

@@ -5,9 +5,16 @@
 // speed and accuracy are both quoted relative to native FP32), plus the
 // C = beta*C kernel used for K == 0 or alpha == 0.
 //
-// Same persistent, XCD-aware 128x128 tiling as the emulated kernel; operand
-// tiles are staged through registers into padded FP32 LDS rows.
+// Two kernels, both persistent over XCD-aware lists of 128x128 tiles:
+//   * gemm_f32_pp_kernel (k-contiguous, 16-byte addressable A: the forward
+//     and input-gradient GEMMs): the two-group, turn-taking structure of the
+//     emulated kernel, with A copied straight to LDS by direct loads and
+//     op(B) packed once per call (pack_b_f32_kernel) into the chunk layout
+//     the kernel copies from;
+//   * gemm_f32_kernel (any other A): operand tiles staged through registers
+//     into padded FP32 LDS rows, one barrier per k-step.
 #include "emu_tile.h"
+#include "emu_walk.h"
 
 namespace emu {
 namespace {
@@ -201,6 +208,363 @@ __global__ __launch_bounds__(GEO::NT, 2) void gemm_f32_kernel(Params p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// FP32 chunk layout of the turn-taking kernel, in LDS and (for op(B)) in the
+// packed workspace: per (tile, k-step) 128 rows of 32 floats (128 bytes, no
+// padding); the eight 16-byte groups of row r (k = 4c .. 4c+3 in group c)
+// are stored in the order c ^ f32_swz(r).  A fragment read (ds_read_b128,
+// lane l: row l % 32, one group) is served 16 lanes at a time from 64 banks
+// of 4 bytes; rows r and r+1 sit in different halves of the banks, and
+// f32_swz gives each pair of rows among 16 a different group position, so
+// the 16 lanes hit 16 disjoint 16-byte bank groups.
+// ---------------------------------------------------------------------------
+constexpr int F32_CHUNK = TILE * BK;   // floats per chunk: 16 KB
+
+__host__ __device__ constexpr int f32_swz(int r) { return (r >> 1) & 7; }
+__host__ __device__ constexpr int f32_elem(int r, int k)
+{
+    return r * BK + ((((k >> 2) ^ f32_swz(r)) << 2) | (k & 3));
+}
+
+// op(B) (element (k, n) = B[n*ld + k] when kc, else B[k*ld + n]) into chunks
+// [n-tile][k-step][128 n][32 k] of the layout above, zero outside op(B).
+// One thread per (n, 4-wide k group) of the padded extent; consecutive
+// threads walk the contiguous index of B.
+__global__ void pack_b_f32_kernel(const float* __restrict__ B, int64_t ld, int kc, int64_t N, int64_t K,
+                                  int tiles_n, int nk, float* __restrict__ W)
+{
+    const int64_t npad = (int64_t)tiles_n * TILE;
+    const int64_t kgroups = (int64_t)nk * (BK / 4);
+    const int64_t total = npad * kgroups;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        int64_t n, kg;
+        if (kc) {
+            n = idx / kgroups;
+            kg = idx - n * kgroups;
+        } else {
+            kg = idx / npad;
+            n = idx - kg * npad;
+        }
+        const int64_t k0 = kg * 4;
+        f32x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t k = k0 + e;
+            v[e] = (n < N && k < K) ? (kc ? B[n * ld + k] : B[k * ld + n]) : 0.0f;
+        }
+        const int64_t tn = n / TILE, rr = n - tn * TILE;
+        const int64_t kt = k0 / BK, kk = k0 - kt * BK;
+        *reinterpret_cast<f32x4_t*>(W + (tn * nk + kt) * F32_CHUNK + f32_elem((int)rr, (int)kk)) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Native FP32 GEMM in the turn-taking form.  The 8 waves form two groups of
+// four, one wave of each per SIMD; group g owns rows 64g..64g+63 of the
+// 128x128 tile, each of its waves a 64x32 block (two 32x32 MFMA tiles of
+// v_mfma_f32_32x32x2_f32).  Each group alternates two phases, each closed by
+// a workgroup barrier, and group 1 runs one phase behind group 0, so that on
+// every SIMD one wave issues MFMAs while the other loads and stores:
+//   U(s): direct loads of the group's half of a B chunk (group 0: step s+1,
+//         group 1: step s+2) and of its own A rows of step s+2; the
+//         epilogue of the tile that ended at step s-1 (stores after the
+//         loads); the first operand fragments of M(s);
+//   M(s): 32 MFMAs on the step-s A rows (LDS stage s % 3) and B chunk
+//         (buffer s % 3), the cursor advances, then the wait for the loads
+//         of U(s-1) (A rows of step s+1) and U(s) (B half), and on a step
+//         whose k runs past K the zeroing of the A groups past K.
+// A's k-groups past K were loaded from column 0 of the row (a valid
+// address) and are zeroed in LDS by the thread that loaded them, after its
+// own wait, so the products past K are exactly zero (B is zero there too).
+// Rows past M re-read the last row and only feed outputs that are not
+// stored.  LDS: three A stages and three B chunk buffers, 96 KB.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512, 1) void gemm_f32_pp_kernel(Params p, const float* __restrict__ Wb)
+{
+    constexpr int GT = 256;                                // threads per group
+    constexpr int GROWS = TILE / 2;                        // A rows per group
+    constexpr int CHUNK_BYTES = F32_CHUNK * 4;
+    constexpr int B_ROUNDS = CHUNK_BYTES / (GT * 16);      // 4 KB rounds per B chunk
+    constexpr int B_HALF = B_ROUNDS / 2;                   // rounds each group copies
+    constexpr int A_ROUNDS = GROWS * BK * 4 / (GT * 16);   // 16-byte loads per thread
+    constexpr int TM = 2;
+    static_assert(A_ROUNDS == 2 && GROWS == 2 * 32, "thread t loads rows t/8 and t/8 + 32 of its group");
+    static_assert(B_ROUNDS * GT * 16 == CHUNK_BYTES && B_HALF * 2 == B_ROUNDS, "B chunk in whole half rounds");
+    __shared__ __attribute__((aligned(16))) float stage[3][F32_CHUNK];
+    __shared__ __attribute__((aligned(16))) float smB[3][F32_CHUNK];
+
+    const int G = gridDim.x;
+    const int slot = xcd_position(blockIdx.x, G);
+    const int my_items = (p.ntiles - slot + G - 1) / G;
+    const int total = my_items * p.nk;
+
+    WalkConst wc;
+    const int gtile = G % p.ntiles;
+    wc.nk = p.nk;
+    wc.nk_item = p.nk;
+    wc.tiles_n = p.tiles_n;
+    wc.gtn = gtile % p.tiles_n;
+    wc.gm = (int64_t)(gtile / p.tiles_n) * TILE;
+    wc.gseg = 0;
+    wc.mrows = (int64_t)(p.ntiles / p.tiles_n) * TILE;
+    wc.tail_k = (int)(p.K - (int64_t)(p.nk - 1) * BK);
+    wc.M = p.M;
+    wc.lda = p.lda;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
+    const int grp = wave >> 2;
+    const int gw = wave & 3;          // wave within the group = its 32-column block
+    const int gt = t & (GT - 1);
+    const int frag_row = lane & 31;
+    const int frag_h = lane >> 5;     // lane half: k = 16 h .. 16 h + 15 of a step
+
+    // Thread gt of group g loads rows 64g + gt/8 + 32r (r = 0, 1) of each A
+    // step.  Its direct load lands at group position gt % 8 of the row, so
+    // it reads the k-group stored there: (gt % 8) ^ f32_swz(row), the same
+    // for both rows.
+    const int srow0 = GROWS * grp + (gt >> 3);
+    const int spos = gt & 7;
+    const int skc = 4 * (spos ^ f32_swz(srow0));
+    uint32_t a_off[A_ROUNDS];
+#pragma unroll
+    for (int r = 0; r < A_ROUNDS; ++r)
+        a_off[r] = (uint32_t)(((int64_t)(srow0 + 32 * r) * p.lda + skc) * 4);
+
+    // Round r of the group's A rows of step w into stage sb: this wave's 64
+    // lanes fill the 1 KB at row 64g + 8 gw + 32 r.
+    auto copy_a = [&](const Walk& w, int sb) __attribute__((always_inline)) {
+        const float* base = p.A + w.arow + (int64_t)w.kt * BK;
+        const uint32_t dst = lds_offset(stage[sb]) + 8192 * grp + 1024 * gw;
+#pragma unroll
+        for (int r = 0; r < A_ROUNDS; ++r) {
+            uint32_t off = a_off[r];
+            if (w.rows != TILE || w.kvalid != BK) {
+                const int row = srow0 + 32 * r;
+                const int64_t rr = row < w.rows ? row : w.rows - 1;
+                const int kk = skc < w.kvalid ? skc : 0;
+                off = (uint32_t)((rr * p.lda + kk) * 4);
+            }
+            copy16_to_lds(dst + 4096 * r, base, off);
+        }
+    };
+    // After this thread's load of step w into stage sb has landed: its
+    // k-groups past K become zero.
+    auto zero_tail = [&](const Walk& w, int sb) __attribute__((always_inline)) {
+        if (skc >= w.kvalid) {
+#pragma unroll
+            for (int r = 0; r < A_ROUNDS; ++r)
+                *reinterpret_cast<f32x4_t*>(&stage[sb][(srow0 + 32 * r) * BK + 4 * spos]) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    };
+    // This group's half of the B chunk of step w into buffer bb: rounds
+    // B_HALF g .. B_HALF g + B_HALF - 1, round r the 4 KB at 4096 r, this
+    // wave's 1 KB piece of it at 4096 r + 1024 gw.
+    auto copy_b_half = [&](const Walk& w, int bb) __attribute__((always_inline)) {
+        const char* src = reinterpret_cast<const char*>(Wb + ((int64_t)w.tn * p.nk + w.kt) * F32_CHUNK);
+        const uint32_t dst = lds_offset(smB[bb]);
+#pragma unroll
+        for (int j = 0; j < B_HALF; ++j) {
+            const int byte0 = ((grp * B_HALF + j) * GT + gw * 64) * 16;
+            copy16_to_lds(dst + byte0, src + byte0, (uint32_t)lane * 16);
+        }
+    };
+
+    f32x16_t acc[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) acc[i] = zero_acc();
+
+    // Fragments of k-group 4h + q (q = 0..3) of this lane's row l % 32 of a
+    // 32-row block: the block's rows start at multiples of 32, where f32_swz
+    // repeats, so the offset within the block is the same for every block.
+    const int fsw = f32_swz(frag_row);
+    auto foff = [&](int q) __attribute__((always_inline)) { return frag_row * BK + (((4 * frag_h + q) ^ fsw) << 2); };
+    auto load_frags = [&](int bb, int q, f32x4_t& bf, f32x4_t (&af)[TM]) __attribute__((always_inline)) {
+        bf = *reinterpret_cast<const f32x4_t*>(&smB[bb][gw * 32 * BK + foff(q)]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            af[i] = *reinterpret_cast<const f32x4_t*>(&stage[bb][(grp * GROWS + i * 32) * BK + foff(q)]);
+    };
+
+    // Epilogue of this wave's 64x32 block of the tile at w: C = alpha t +
+    // beta C + bias.  Lane l holds, per 32x32 block and register group q,
+    // row l%32 and columns 8q + 4(l/32) .. +3 (B is the MFMAs' first
+    // operand): one 16-byte buffer store each, rows outside C given an
+    // out-of-range offset.  Tiles that cross column N, or a C without
+    // 16-byte rows, store element by element.  Returns whether the vector
+    // path ran: then the epilogue's last EPI_STORES vector memory operations
+    // are its stores.
+    constexpr int EPI_STORES = TM * 4;
+    auto epilogue = [&]<bool SCALE>(const TilePos& w) __attribute__((always_inline)) {
+        const int64_t n0 = (int64_t)w.tn * TILE;
+        float* const dst = p.C + w.m0 * p.ldc + n0;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, 0x7FFFFFFF, 0x00020000);
+        const int64_t cl = p.N - n0;
+        const int cols_left = cl < TILE ? (int)cl : TILE;
+        const bool vec_c = p.vec_b != 0 && cols_left == TILE;
+        const int ldc4 = (int)p.ldc * 4;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = grp * GROWS + i * 32 + (lane & 31);
+            const bool row_ok = row < w.rows;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = gw * 32 + 8 * q + 4 * (lane >> 5);
+                f32x4_t out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = SCALE ? p.alpha * acc[i][4 * q + e] : acc[i][4 * q + e];
+                if (vec_c) {
+                    const int off = row_ok ? row * ldc4 + col * 4 : (int)0x80000000;
+                    if (p.beta != 0.0f) {
+                        const f32x4_t old = __builtin_bit_cast(
+                            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(p.beta, old[e], out[e]);
+                    }
+                    if (p.bias != nullptr) {
+                        // the wave's 8 bias values of group q, one scalar load
+                        const i32x8_t bv = scalar_load8(p.bias + n0 + gw * 32 + 8 * q);
+                        const bool upper = (lane >> 5) != 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            int lo = bv[e], hi = bv[4 + e];
+                            asm("" : "+s"(lo));
+                            asm("" : "+s"(hi));
+                            out[e] = out[e] + __int_as_float(upper ? hi : lo);
+                        }
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, out), rsrc, off, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (row_ok && col + e < cols_left) {
+                            float* cp = dst + row * p.ldc + col + e;
+                            float o = out[e];
+                            if (p.beta != 0.0f) o = __builtin_fmaf(p.beta, *cp, o);
+                            if (p.bias != nullptr) o = o + p.bias[n0 + col + e];
+                            *cp = o;
+                        }
+                    }
+                }
+            }
+        }
+        return vec_c;
+    };
+    const bool unit_alpha = p.alpha == 1.0f;
+    auto epilogue_any = [&](const TilePos& w) __attribute__((always_inline)) {
+        return unit_alpha ? epilogue.template operator()<false>(w) : epilogue.template operator()<true>(w);
+    };
+
+    // Cursors: wm = step of the next M phase, we = the step before it, ws =
+    // the step after it, wa = two steps after it (its A rows loaded in the
+    // next U phase).
+    Walk wm;
+    wm.seg = 0;
+    wm.tn = slot % p.tiles_n;
+    wm.m0 = (int64_t)(slot / p.tiles_n) * TILE;
+    wm.left = my_items - 1;
+    walk_start_segment(wm, wc);
+    walk_set_tile(wm, wc);
+    wm.kvalid = wm.kt + 1 < p.nk ? BK : wc.tail_k;
+    Walk ws = wm, wa = wm;
+    TilePos we{wm.m0, wm.tn, wm.rows, wm.seg};
+    // Prologue: B chunk of step 0 (each group its half) and group 1's half
+    // of chunk 1; A rows of steps 0 and 1 (stages 0 and 1).
+    copy_b_half(ws, 0);
+    copy_a(wa, 0);
+    walk_next<false>(wa, wc);
+    copy_a(wa, 1);
+    walk_next<false>(wa, wc);
+    walk_next<false>(ws, wc);
+    if (grp == 1) copy_b_half(ws, 1);
+    wait_vmcnt<0>();
+    if (wm.kvalid != BK) zero_tail(wm, 0);   // (step 1's tail is zeroed at the end of M(0))
+    __syncthreads();
+    if (grp == 1) __builtin_amdgcn_s_barrier();   // group 1 runs one phase behind group 0
+
+    const bool reads_c = p.beta != 0.0f;
+    bool epi = false;       // U(s) runs the epilogue of step s-1's tile
+    bool stores = false;    // the last U phase ended with EPI_STORES stores
+    int bm = 0;             // A stage and B buffer of step s: s % 3
+    for (int s = 0; s < total; ++s) {
+        const int bn = bm == 2 ? 0 : bm + 1;    // step s+1
+        const int bn2 = bn == 2 ? 0 : bn + 1;   // step s+2
+        // ---- U(s).  An epilogue that reads C runs before the loads: the
+        // compiler's waits for its C loads would also wait for direct loads
+        // issued before them.
+        if (epi && reads_c) {
+            epilogue_any(we);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) acc[i] = zero_acc();
+        }
+        // Group 0 loads its half of B chunk s+1 into the buffer of step
+        // s-2, group 1 its half of chunk s+2 into that of step s-1; the A
+        // rows of step s+2 go to the group's rows of stage s-1.  The last
+        // readers of each (M(s-2) of both groups, M(s-1) of both groups,
+        // M(s-1) of this group) ended before this phase.
+        if (grp == 0)
+            copy_b_half(ws, bn);
+        else
+            copy_b_half(wa, bn2);
+        copy_a(wa, bn2);
+        stores = false;
+        if (epi && !reads_c) {
+            stores = epilogue_any(we);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) acc[i] = zero_acc();
+        }
+        // First fragments of M(s): A rows of step s (landed and zeroed past K
+        // before the barrier that ended M(s-1)) and B chunk s (both halves
+        // landed before the barrier that ended the phase before U0(s)).
+        f32x4_t bq[2], aq[2][TM];
+        load_frags(bm, 0, bq[0], aq[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- M(s): k-groups q = 0..3 of each lane half, the fragments of
+        // group q+1 read while group q issues.  MFMA 4q + e sums the k pair
+        // (4q + e, 16 + 4q + e).
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q + 1 < 4) load_frags(bm, q + 1, bq[(q + 1) & 1], aq[(q + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    // B operand first: lane l then holds row l%32 of the
+                    // block and four consecutive columns per register group
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(bq[q & 1][e], aq[q & 1][i][e], acc[i], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        epi = wm.kt == p.nk - 1;
+        we = TilePos{wm.m0, wm.tn, wm.rows, wm.seg};
+        wm = ws;
+        ws = wa;
+        walk_next<false>(wa, wc);
+        bm = bn;
+        // Before the next barrier: this group's half of B loaded in U(s) and
+        // its A rows of step s+1 (loaded in U(s-1)) have landed, while its A
+        // load of U(s) and the epilogue's stores, issued after them, may
+        // still be in flight; then the A groups of step s+1 past K are zeroed.
+        if (stores)
+            wait_vmcnt<A_ROUNDS + EPI_STORES>();
+        else
+            wait_vmcnt<A_ROUNDS>();
+        if (wm.kvalid != BK) zero_tail(wm, bm);
+        wait_lgkmcnt0();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    epilogue_any(we);
+    wait_vmcnt<0>();   // no direct load may still be writing LDS when the workgroup ends
+    if (grp == 0) __builtin_amdgcn_s_barrier();   // matches group 1's extra barrier
+}
+
 __global__ void scale_c_kernel(int64_t M, int64_t N, float beta, float* __restrict__ C,
                                int64_t ldc, const float* __restrict__ bias)
 {
@@ -257,8 +621,51 @@ using GeoF32 = Geo<2, 2, 2, 2>;     // 4 waves, each 64x64: 128x128 per workgrou
 
 }  // namespace
 
-hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, hipStream_t stream)
+// The turn-taking kernel applies to a k-contiguous, 16-byte addressable A
+// (as the emulated kernel's fused path) whose tile and chunk counts fit its
+// 32-bit arithmetic.
+bool native_pp_path(const GemmArgs& g)
 {
+    const int64_t tiles_m = (g.M + TILE - 1) / TILE;
+    const int64_t tiles_n = (g.N + TILE - 1) / TILE;
+    const int64_t nk = (g.K + BK - 1) / BK;
+    const int64_t lim = (int64_t)1 << 31;
+    return fused_a_path(g) && tiles_m * tiles_n < lim && tiles_m * tiles_n * nk < lim && tiles_n * nk < lim;
+}
+
+size_t gemm_native_f32_workspace_bytes(const GemmArgs& g)
+{
+    if (!native_pp_path(g)) return 0;
+    const int64_t tiles_n = (g.N + TILE - 1) / TILE;
+    const int64_t nk = (g.K + BK - 1) / BK;
+    return ((size_t)(tiles_n * nk * F32_CHUNK) * sizeof(float) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, void* workspace,
+                                  hipStream_t stream)
+{
+    if (native_pp_path(g)) {
+        if (workspace == nullptr || ((uintptr_t)workspace & 15u) != 0) return hipErrorInvalidValue;
+        Params p = make_params(g, TILE, TILE);
+        p.ksplit = 1;
+        p.nk_item = p.nk;
+        // (turn-taking kernel) C rows allow 16-byte stores at 16-byte aligned
+        // columns, and the bias (if any) 16-byte loads there
+        p.vec_b = (((uintptr_t)g.C & 15u) == 0 && (g.ldc & 3) == 0 &&
+                   (g.bias == nullptr || ((uintptr_t)g.bias & 15u) == 0) &&
+                   (int64_t)TILE * g.ldc * 4 < ((int64_t)1 << 31)) ? 1 : 0;
+        float* W = static_cast<float*>(workspace);
+        const int64_t work = (int64_t)p.tiles_n * TILE * p.nk * (BK / 4);
+        int64_t blocks = (work + 255) / 256;
+        if (blocks > 16384) blocks = 16384;
+        hipLaunchKernelGGL(pack_b_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g.B, g.ldb,
+                           g.trans_b ? 1 : 0, g.N, g.K, p.tiles_n, p.nk, W);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int grid = p.ntiles < dev.num_cu ? p.ntiles : dev.num_cu;
+        hipLaunchKernelGGL(gemm_f32_pp_kernel, dim3(grid), dim3(512), 0, stream, p, W);
+        return hipGetLastError();
+    }
     if (!fits_32bit(g, GeoF32::BM, GeoF32::BN)) return hipErrorInvalidValue;
     const Params p = make_params(g, GeoF32::BM, GeoF32::BN);
     const int cap = 2 * dev.num_cu;

@@ -44,7 +44,12 @@ bool fused_a_path(const GemmArgs& g);
 size_t gemm_bf16_workspace_bytes(const GemmArgs& g, int nbands, int ksplit);
 hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const DeviceInfo& dev,
                             void* workspace, hipStream_t stream);
-hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, hipStream_t stream);
+// The native FP32 GEMM: its device workspace (bytes, a multiple of 256; 0
+// when the call takes the kernel that needs none) and the launch with it
+// (`workspace` 16-byte aligned, used in stream order only).
+size_t gemm_native_f32_workspace_bytes(const GemmArgs& g);
+hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, void* workspace,
+                                  hipStream_t stream);
 // The BF16 planes of op(B) (K x N; element (k, n) is B[n*ldb + k] when
 // trans_b, else B[k*ldb + n]) in the layout the emulated kernels read:
 // their size in bytes, and the split into `planes` (16-byte aligned) for

@@ -25,7 +25,9 @@ struct Params {
     int ntiles;    // output tiles in total
     int nk;        // k-steps per tile
     int vec_a;     // op(A) rows may be read with 16-byte loads
-    int vec_b;     // op(B) columns may be read with 16-byte loads (native kernel)
+    // gemm_f32_kernel: op(B) columns may be read with 16-byte loads; kernels
+    // with the 16-byte epilogue: C rows (and the bias) allow 16-byte access
+    int vec_b;
     // Split of K into ksplit equal segments of nk_item k-steps (fused-A
     // kernel only; 1: none).  With ksplit > 1 the kernel writes each
     // (segment, tile) result t, unscaled, to wsC[seg][M][N] (vec_ws: 16-byte

@@ -339,3 +339,70 @@ def test_auto_matches_selected_mode():
         chosen = emu.select_mode(M, N, K)
         say(f"AUTO {M}x{N}x{K} -> {chosen}")
         assert np.array_equal(run(a, b, "AUTO"), run(a, b, chosen))
+
+
+def test_inf_in_first_column_ragged_k():
+    """Inf in column 0 of A with K not a multiple of 32: k past K must add
+    exact zeros (the direct-load paths fill that part of the last k-step from
+    column 0 and then zero it).  NATIVE_F32: the row is exactly the FP64
+    result, +-Inf (B[0, j] != 0), not NaN.  The emulated modes split Inf into
+    (Inf, 0, 0), whose products with B's pieces give Inf or NaN: there the
+    row must be non-finite and the others finite."""
+    rng = np.random.default_rng(12)
+    for K in (36, 100, 260):
+        a = rng.standard_normal((130, K)).astype(np.float32)
+        b = rng.standard_normal((K, 140)).astype(np.float32)
+        a[7, 0] = np.inf
+        a[128, 0] = -np.inf
+        with np.errstate(invalid="ignore", over="ignore"):
+            ref = oracle.gemm_f64(a, b)
+        for mode in MODES:
+            say(f"inf column 0 K={K} {mode}")
+            out = run(a, b, mode)
+            for r in (7, 128):
+                if mode == "NATIVE_F32":
+                    assert np.array_equal(out[r], ref[r].astype(np.float32)), (mode, K, r)
+                else:
+                    assert not np.isfinite(out[r]).any(), (mode, K, r)
+            others = np.delete(out, [7, 128], axis=0)
+            assert np.isfinite(others).all(), (mode, K)
+
+
+@pytest.mark.parametrize("tb", [False, True])
+def test_native_kernels_agree_bitwise(tb):
+    """The native FP32 path has two kernels: the turn-taking one for a
+    k-contiguous, 16-byte addressable A and the register-staged one for any
+    other A (here: the same A one float off 16-byte alignment).  Both form
+    every MFMA from the same k pair in the same order, so they agree bit for
+    bit, on full and ragged tiles and with alpha, beta and a bias."""
+    import torch
+
+    import emulated_fp32_matrix_amd as emu
+
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(13)
+    for M, N, K in [(256, 256, 256), (300, 200, 100), (129, 385, 36), (1000, 128, 768)]:
+        a = rng.standard_normal((M, K)).astype(np.float32)
+        b_op = rng.standard_normal((K, N)).astype(np.float32)
+        B = _store(b_op, tb)
+        c0 = rng.standard_normal((M, N)).astype(np.float32)
+        bias = rng.standard_normal(N).astype(np.float32)
+        bd = torch.from_numpy(np.ascontiguousarray(B)).to(dev)
+        biasd = torch.from_numpy(bias).to(dev)
+        abuf = torch.zeros(M * K + 4, dtype=torch.float32, device=dev)
+        abuf[4:] = torch.from_numpy(a.ravel()).to(dev)   # 16-byte aligned copy
+        abuf2 = torch.zeros(M * K + 1, dtype=torch.float32, device=dev)
+        abuf2[1:] = torch.from_numpy(a.ravel()).to(dev)  # 4 bytes off alignment
+        outs = []
+        for ptr in (abuf.data_ptr() + 16, abuf2.data_ptr() + 4):
+            for alpha, beta, use_bias in [(1.0, 0.0, False), (-0.75, 1.5, True)]:
+                cd = torch.from_numpy(c0).to(dev)
+                say(f"native kernels {M}x{N}x{K} tb={tb} alpha={alpha} beta={beta} ptr%16={ptr % 16}")
+                st = emu.emu_sgemm_bias(0, int(tb), M, N, K, alpha, ptr, K, bd.data_ptr(), B.shape[1], beta,
+                                        cd.data_ptr(), N, biasd.data_ptr() if use_bias else 0, "NATIVE_F32",
+                                        torch.cuda.current_stream().cuda_stream)
+                assert st == emu.STATUS_SUCCESS
+                torch.cuda.synchronize()
+                outs.append(cd.cpu().numpy())
+        assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3]), (M, N, K, tb)
+        check_result(outs[0], oracle.gemm_f64(a, b_op), a, b_op, "NATIVE_F32", label=f"native {M}x{N}x{K}")
