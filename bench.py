@@ -61,6 +61,7 @@ def parse():
 # Source files that determine the code of the emulated GEMM kernels.
 KERNEL_SOURCES = ("emulated_fp32_matrix_amd/csrc/emu_gemm_bf16.hip",
                   "emulated_fp32_matrix_amd/csrc/emu_tile.h",
+                  "emulated_fp32_matrix_amd/csrc/emu_walk.h",
                   "emulated_fp32_matrix_amd/csrc/emu_device.h")
 
 # HBM traffic per launch of the main BF16X9 GEMM kernel over this workload

@@ -86,30 +86,27 @@ def measure(modes=("NATIVE_F32", "BF16X9")):
 
 
 # ---- the cost model (same form as predict_x9_us / predict_us in csrc/emu_api.hip) ----
-PARAMS = ("x9_fixed", "x9_step_part", "x9_step_full", "f32_fixed", "f32_step1", "f32_step2")
+PARAMS = ("x9_fixed", "x9_step_part", "x9_step_full", "f32_fixed", "f32_step_part", "f32_step_full")
 
 
 def predict(M, N, K, p):
-    """(native, BF16X9 unsplit) predicted device time in microseconds: the
-    emulated kernel runs ceil(tiles / 256) rounds of nk k-steps, each step
-    costing x9_step_full once every CU has a tile and x9_step_part before;
-    the native kernel one tile per CU up to 256 tiles, two beyond."""
+    """(native, BF16X9 unsplit) predicted device time in microseconds: both
+    kernels keep one 128x128 tile per CU and run ceil(tiles / 256) rounds of
+    nk k-steps, each step costing *_step_full once every CU has a tile and
+    *_step_part before."""
     tiles = math.ceil(M / 128) * math.ceil(N / 128)
     nk = math.ceil(K / 32)
-    step = p["x9_step_full"] if tiles >= 256 else p["x9_step_part"]
-    x9 = p["x9_fixed"] + math.ceil(tiles / 256) * nk * step
-    if tiles <= 256:
-        f32 = p["f32_fixed"] + nk * p["f32_step1"]
-    else:
-        f32 = p["f32_fixed"] + math.ceil(tiles / 512) * nk * p["f32_step2"]
+    full = tiles >= 256
+    x9 = p["x9_fixed"] + math.ceil(tiles / 256) * nk * (p["x9_step_full"] if full else p["x9_step_part"])
+    f32 = p["f32_fixed"] + math.ceil(tiles / 256) * nk * (p["f32_step_full"] if full else p["f32_step_part"])
     return f32, x9
 
 
 def fit(rows):
     from scipy.optimize import minimize
 
-    start = dict(x9_fixed=22.0, x9_step_part=1.2, x9_step_full=2.1, f32_fixed=10.0,
-                 f32_step1=3.0, f32_step2=5.9)
+    start = dict(x9_fixed=12.0, x9_step_part=1.4, x9_step_full=2.0, f32_fixed=12.0,
+                 f32_step_part=2.2, f32_step_full=2.3)
 
     def loss(v):
         p = dict(zip(PARAMS, v))

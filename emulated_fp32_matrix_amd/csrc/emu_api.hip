@@ -147,22 +147,21 @@ bool valid_op(int op) { return op == EMU_OP_N || op == EMU_OP_T; }
 int64_t max1(int64_t v) { return v > 1 ? v : 1; }
 
 // Cost model of one call on MI355X: predicted device time in microseconds,
-// including the B pre-split of the emulated path (its workspace comes from
-// the per-stream cache).  Its form follows the kernels: 128x128 output tiles, K in steps of
-// 32; the emulated kernel keeps one (tile or K-segment) item per CU (256 at
-// a time), and a k-step costs more once every CU is busy (the clock is then
-// power-limited); the native kernel runs one tile per CU up to 256 tiles and
-// two per CU beyond.  The constants are a least-squares fit (log error) to
-// device times measured with emulated_fp32_matrix_amd/calibrate.py over 67
-// shapes: the MLIP layer stacks, squares 128..8192, skinny shapes and a K
-// sweep.  On those shapes the choice is the faster mode in 66 of 67 cases
-// and within 12 % of it in the other.
-constexpr double kX9Fixed = 11.59;       // us: pre-split launch, pipeline fill
-constexpr double kX9StepPart = 1.431;    // us per k-step per round while some CUs are idle
-constexpr double kX9StepFull = 1.984;    // us per k-step per round with every CU busy
-constexpr double kF32Fixed = 10.586;
-constexpr double kF32Step1 = 3.057;      // us per k-step, one tile per CU
-constexpr double kF32Step2 = 5.840;      // us per k-step per round of two tiles per CU
+// including the B pre-split (emulated) or pack (native) of each path (their
+// workspace comes from the per-stream cache).  Its form follows the kernels:
+// 128x128 output tiles, K in steps of 32; both kernels keep one (tile or
+// K-segment) item per CU (256 at a time), and a k-step costs more once every
+// CU is busy.  The constants are a least-squares fit (log error) to device
+// times measured with emulated_fp32_matrix_amd/calibrate.py over 67 shapes:
+// the MLIP layer stacks, squares 128..8192, skinny shapes and a K sweep.  On
+// those shapes the choice is the faster mode in 65 of 67 cases and within
+// 1 % of it in the other two.
+constexpr double kX9Fixed = 11.519;      // us: pre-split launch, pipeline fill
+constexpr double kX9StepPart = 1.4118;   // us per k-step per round while some CUs are idle
+constexpr double kX9StepFull = 1.9740;   // us per k-step per round with every CU busy
+constexpr double kF32Fixed = 10.986;     // us: B pack launch, pipeline fill
+constexpr double kF32StepPart = 2.0028;
+constexpr double kF32StepFull = 2.4815;
 constexpr double kCUs = 256.0;
 // A split K (S segments of ceil(K/32)/S k-steps each) runs S times as many
 // (segment, tile) items with 1/S of the k-steps each, then a reduction
@@ -212,8 +211,7 @@ void predict_us(int64_t M, int64_t N, int64_t K, double& f32, double& x9)
     const double tiles = ceil_div((double)M, 128.0) * ceil_div((double)N, 128.0);
     const double nk = ceil_div((double)K, 32.0);
     x9 = predict_x9_us(M, N, K, choose_ksplit(M, N, K));
-    f32 = tiles <= kCUs ? kF32Fixed + nk * kF32Step1
-                        : kF32Fixed + ceil_div(tiles, 2.0 * kCUs) * nk * kF32Step2;
+    f32 = kF32Fixed + ceil_div(tiles, kCUs) * nk * (tiles >= kCUs ? kF32StepFull : kF32StepPart);
 }
 
 emu_mode_t select_mode(int64_t M, int64_t N, int64_t K)
