@@ -69,7 +69,7 @@ KERNEL_SOURCES = ("emulated_fp32_matrix_amd/csrc/emu_gemm_bf16.hip",
 # WRITE_SIZE) scaled by the same counters' reading for a 1 GiB device copy.
 # Keyed by the SHA-256 of KERNEL_SOURCES: a changed kernel reports null.
 TRAFFIC_BY_SOURCE = {
-    "ec09c45601f0d158806d74a24a5ba7baf4f7d9b384b2a1bb706ebcd26d53311f": 1858746995,
+    "9221ac1dcae82b7dcb8a9e379adecd2fcc94a3d4697b1c6874df8499752f144e": 1856822182,
 }
 
 
