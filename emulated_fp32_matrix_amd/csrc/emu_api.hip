@@ -343,7 +343,7 @@ const char* emu_status_string(emu_status_t status)
     }
 }
 
-int emu_abi_version(void) { return 104; }
+int emu_abi_version(void) { return 105; }
 
 emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
                               emu_mode_t* chosen)

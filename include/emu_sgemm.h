@@ -31,7 +31,10 @@
  *     for B: planes * 2 bytes * ceil(N/128)*128 * ceil(K/32)*32 (3 planes,
  *     2 in BF16X3, 1 in BF16X1),
  *     likewise with M for A; S * M * N * 4 bytes for a split into S
- *     segments.  The library keeps one workspace per (device, stream): a
+ *     segments.  NATIVE_F32 needs one for op(B) packed as FP32, 4 bytes *
+ *     ceil(N/128)*128 * ceil(K/32)*32, when A is k-contiguous and 16-byte
+ *     addressable (transA == N, A 16-byte aligned, lda and K multiples of
+ *     4), and none otherwise.  The library keeps one workspace per (device, stream): a
  *     buffer that grows to the largest size a call on that stream has needed
  *     and is used only by calls on that stream, so in its order.  It is
  *     allocated on the stream from a memory pool the library creates once
@@ -39,8 +42,8 @@
  *     creating one fails); growing frees the old buffer with hipFreeAsync on
  *     the stream.  Up to 16 streams per device keep a buffer; beyond that the
  *     least recently used one is released with hipFree, which waits for the
- *     device.  The buffers live until the process ends.  NATIVE_F32 and
- *     emu_split_bf16x3 allocate nothing.
+ *     device.  The buffers live until the process ends.  emu_split_bf16x3
+ *     allocates nothing.
  *   - stream is a hipStream_t (NULL = the null stream).  Work is enqueued on
  *     it asynchronously; errors during execution surface at the caller's
  *     next synchronisation of that stream.
@@ -119,8 +122,9 @@ typedef enum {
  * Errors: EMU_STATUS_INVALID_VALUE for M, N or K < 0, a leading dimension
  * below its bound, a NULL A or B with M*N*K > 0, a NULL C with M*N > 0, or a
  * transA/transB/mode outside its enum.  EMU_STATUS_NOT_SUPPORTED if the
- * current device is not gfx950.  EMU_STATUS_ALLOC_FAILED if the BF16X*
- * workspace allocation fails (nothing was launched).  EMU_STATUS_LAUNCH_FAILED
+ * current device is not gfx950.  EMU_STATUS_ALLOC_FAILED if the stream's
+ * workspace cannot be allocated or grown (nothing was launched).
+ * EMU_STATUS_LAUNCH_FAILED
  * if a launch reports an error.
  */
 emu_status_t emu_sgemm(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
@@ -271,10 +275,11 @@ emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64
  * codes give "EMU_STATUS_UNKNOWN".  Never NULL. */
 const char* emu_status_string(emu_status_t status);
 
-/* ABI version of this header (major * 100 + minor): 104 (1.1 added
+/* ABI version of this header (major * 100 + minor): 105 (1.1 added
  * emu_sgemm_bias, 1.2 EMU_MODE_BF16X1, 1.3 emu_sgemm_ex and
  * emu_sgemm_ksplit, 1.4 emu_presplit_b_bytes, emu_presplit_b and
- * emu_sgemm_presplit). */
+ * emu_sgemm_presplit, 1.5 a stream workspace for NATIVE_F32, which may
+ * therefore return EMU_STATUS_ALLOC_FAILED). */
 int emu_abi_version(void);
 
 #ifdef __cplusplus

@@ -45,7 +45,7 @@ def test_status_strings_and_version():
     assert emu.emu_status_string(2) == "EMU_STATUS_NOT_SUPPORTED"
     assert emu.emu_status_string(3) == "EMU_STATUS_LAUNCH_FAILED"
     assert emu.emu_status_string(99) == "EMU_STATUS_UNKNOWN"
-    assert emu.emu_abi_version() == 104
+    assert emu.emu_abi_version() == 105
 
 
 FAKE = 0x1000  # never dereferenced: validation fails (or returns) before any HIP call
