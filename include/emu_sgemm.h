@@ -43,7 +43,10 @@
  *     the stream.  Up to 16 streams per device keep a buffer; beyond that the
  *     least recently used one is released with hipFree, which waits for the
  *     device.  The buffers live until the process ends.  emu_split_bf16x3
- *     allocates nothing.
+ *     allocates nothing.  The cache knows streams only by their handle:
+ *     synchronise a stream that ran library calls before destroying it, so
+ *     that a new stream that receives the same handle cannot overlap its
+ *     work with the old stream's in the shared buffer.
  *   - stream is a hipStream_t (NULL = the null stream).  Work is enqueued on
  *     it asynchronously; errors during execution surface at the caller's
  *     next synchronisation of that stream.
