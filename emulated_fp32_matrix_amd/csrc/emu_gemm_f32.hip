@@ -266,10 +266,10 @@ __global__ void pack_b_f32_kernel(const float* __restrict__ B, int64_t ld, int k
 // v_mfma_f32_32x32x2_f32).  Each group alternates two phases, each closed by
 // a workgroup barrier, and group 1 runs one phase behind group 0, so that on
 // every SIMD one wave issues MFMAs while the other loads and stores:
-//   U(s): direct loads of the group's half of a B chunk (group 0: step s+1,
-//         group 1: step s+2) and of its own A rows of step s+2; the
-//         epilogue of the tile that ended at step s-1 (stores after the
-//         loads); the first operand fragments of M(s);
+//   U(s): the epilogue of the tile that ended at step s-1; direct loads of
+//         the group's half of a B chunk (group 0: step s+1, group 1: step
+//         s+2) and of its own A rows of step s+2; the first operand
+//         fragments of M(s);
 //   M(s): 32 MFMAs on the step-s A rows (LDS stage s % 3) and B chunk
 //         (buffer s % 3), the cursor advances, then the wait for the loads
 //         of U(s-1) (A rows of step s+1) and U(s) (B half), and on a step
@@ -393,10 +393,7 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_pp_kernel(Params p, const flo
     // row l%32 and columns 8q + 4(l/32) .. +3 (B is the MFMAs' first
     // operand): one 16-byte buffer store each, rows outside C given an
     // out-of-range offset.  Tiles that cross column N, or a C without
-    // 16-byte rows, store element by element.  Returns whether the vector
-    // path ran: then the epilogue's last EPI_STORES vector memory operations
-    // are its stores.
-    constexpr int EPI_STORES = TM * 4;
+    // 16-byte rows, store element by element.
     auto epilogue = [&]<bool SCALE>(const TilePos& w) __attribute__((always_inline)) {
         const int64_t n0 = (int64_t)w.tn * TILE;
         float* const dst = p.C + w.m0 * p.ldc + n0;
@@ -451,11 +448,13 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_pp_kernel(Params p, const flo
                 }
             }
         }
-        return vec_c;
     };
     const bool unit_alpha = p.alpha == 1.0f;
     auto epilogue_any = [&](const TilePos& w) __attribute__((always_inline)) {
-        return unit_alpha ? epilogue.template operator()<false>(w) : epilogue.template operator()<true>(w);
+        if (unit_alpha)
+            epilogue.template operator()<false>(w);
+        else
+            epilogue.template operator()<true>(w);
     };
 
     // Cursors: wm = step of the next M phase, we = the step before it, ws =
@@ -485,17 +484,16 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_pp_kernel(Params p, const flo
     __syncthreads();
     if (grp == 1) __builtin_amdgcn_s_barrier();   // group 1 runs one phase behind group 0
 
-    const bool reads_c = p.beta != 0.0f;
     bool epi = false;       // U(s) runs the epilogue of step s-1's tile
-    bool stores = false;    // the last U phase ended with EPI_STORES stores
     int bm = 0;             // A stage and B buffer of step s: s % 3
     for (int s = 0; s < total; ++s) {
         const int bn = bm == 2 ? 0 : bm + 1;    // step s+1
         const int bn2 = bn == 2 ? 0 : bn + 1;   // step s+2
-        // ---- U(s).  An epilogue that reads C runs before the loads: the
-        // compiler's waits for its C loads would also wait for direct loads
-        // issued before them.
-        if (epi && reads_c) {
+        // ---- U(s).  The epilogue comes first, so its stores issue ahead of
+        // this phase's direct loads instead of queueing behind them (2-3 %
+        // faster than the other order), and the compiler's waits for its C
+        // loads (beta != 0) cover at most the A rows loaded in U(s-1).
+        if (epi) {
             epilogue_any(we);
 #pragma unroll
             for (int i = 0; i < TM; ++i) acc[i] = zero_acc();
@@ -510,12 +508,6 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_pp_kernel(Params p, const flo
         else
             copy_b_half(wa, bn2);
         copy_a(wa, bn2);
-        stores = false;
-        if (epi && !reads_c) {
-            stores = epilogue_any(we);
-#pragma unroll
-            for (int i = 0; i < TM; ++i) acc[i] = zero_acc();
-        }
         // First fragments of M(s): A rows of step s (landed and zeroed past K
         // before the barrier that ended M(s-1)) and B chunk s (both halves
         // landed before the barrier that ended the phase before U0(s)).
@@ -548,12 +540,9 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_pp_kernel(Params p, const flo
         bm = bn;
         // Before the next barrier: this group's half of B loaded in U(s) and
         // its A rows of step s+1 (loaded in U(s-1)) have landed, while its A
-        // load of U(s) and the epilogue's stores, issued after them, may
-        // still be in flight; then the A groups of step s+1 past K are zeroed.
-        if (stores)
-            wait_vmcnt<A_ROUNDS + EPI_STORES>();
-        else
-            wait_vmcnt<A_ROUNDS>();
+        // load of U(s), issued after them, may still be in flight; then the
+        // A groups of step s+1 past K are zeroed.
+        wait_vmcnt<A_ROUNDS>();
         if (wm.kvalid != BK) zero_tail(wm, bm);
         wait_lgkmcnt0();
         __builtin_amdgcn_sched_barrier(0);
