@@ -416,12 +416,10 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 // waves a 64x32 block (two 32x32 MFMA tiles).  Each group alternates two
 // kinds of phase, each closed by a workgroup barrier:
 //   U(s): reads the group's FP32 A rows of step s+1 from staging, then
-//         (while those reads are in flight) issues the direct loads of its
-//         half of a B chunk (group 0: step s+1, group 1: step s+2) and of
-//         its A rows of step s+2,
-//         runs the epilogue of the tile that ended at step s-1 (its stores
-//         issued after the loads, so that waiting for the loads never waits
-//         for them), then splits the step s+1 rows into the other plane
+//         (while those reads are in flight) runs the epilogue of the tile
+//         that ended at step s-1 and issues the direct loads of its half of
+//         a B chunk (group 0: step s+1, group 1: step s+2) and of its A rows
+//         of step s+2, then splits the step s+1 rows into the other plane
 //         buffer;
 //   M(s): the MFMAs of step s, then the scalar bookkeeping (advancing the
 //         step cursors, precomputing addresses) for the next U phase, and
@@ -610,9 +608,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     // columns 8q + 4(l/32) .. +3: one 16-byte buffer store each, rows outside
     // C given an out-of-range offset.  Tiles that cross column N, or a
     // destination without 16-byte rows, store element by element.  SCALE:
-    // alpha != 1.  Returns whether the vector path ran: then the epilogue's
-    // last EPI_STORES vector memory operations are its stores.
-    constexpr int EPI_STORES = TM * 4;
+    // alpha != 1.
     auto epilogue = [&]<bool SCALE, bool PART>(const TilePos& w) __attribute__((always_inline)) {
         const int64_t n0 = (int64_t)w.tn * TILE;
         const int64_t ldd = PART ? p.N : p.ldc;
@@ -683,15 +679,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
                 }
             }
         }
-        return vec_c;
     };
     const bool unit_alpha = p.alpha == 1.0f;
     auto epilogue_any = [&](const TilePos& w) __attribute__((always_inline)) {
         if constexpr (SPLIT)
-            return epilogue.template operator()<false, true>(w);
+            epilogue.template operator()<false, true>(w);
+        else if (unit_alpha)
+            epilogue.template operator()<false, false>(w);
         else
-            return unit_alpha ? epilogue.template operator()<false, false>(w)
-                              : epilogue.template operator()<true, false>(w);
+            epilogue.template operator()<true, false>(w);
     };
 
     // Cursors: wm = step of the next M phase, we = the step before it (its
@@ -733,35 +729,26 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     __syncthreads();
     if (grp == 1) __builtin_amdgcn_s_barrier();   // group 1 runs one phase behind group 0
 
-    // Vector memory operations complete in issue order, so each U phase
-    // issues its loads before the epilogue's stores, and the waits below let
-    // up to EPI_STORES stores stay in flight into the next phase.  An
-    // epilogue that reads C (beta != 0) runs before the loads instead: the
-    // compiler's waits for its own vector loads would also wait for the
-    // direct loads issued before them.  A bias does not need this: the
-    // vector path reads it through the scalar cache (tiles that cross column
-    // N read it element by element and then wait for the direct loads too,
-    // which costs time only).
-    const bool reads_c = !SPLIT && p.beta != 0.0f;
+    // The epilogue runs before the U phase's direct loads: its stores then
+    // issue ahead of those loads instead of queueing behind them (2-3 %
+    // faster than the other order, results identical), and the compiler's
+    // waits for its C loads (beta != 0) find no direct load of this phase
+    // in flight.  Vector memory operations complete in issue order, so the
+    // waits below also cover the stores.
     bool epi = false;       // U(s) runs the epilogue of step s-1's tile
-    bool stores = false;    // the last U phase ended with EPI_STORES stores
     int bm = 0;             // B buffer of step s: s % 3
     for (int s = 0; s < total; ++s) {
         const int b = s & 1;
         const int bn = bm == 2 ? 0 : bm + 1;   // B buffer of step s+1
         // ---- U(s).  The A rows of step s+1 were loaded in U(s-1) (or the
-        // prologue) into staging b^1, after that phase's half of B chunk
-        // s; only that U phase's stores, issued after them, may still be in
-        // flight.
-        if (stores)
-            wait_vmcnt<EPI_STORES>();
-        else
-            wait_vmcnt<0>();
+        // prologue) into staging b^1, after that phase's epilogue stores and
+        // half of B chunk s.
+        wait_vmcnt<0>();
         f32x4_t sv[A_ROUNDS];
         load_rows(ws, b ^ 1, sv);
-        if (epi && reads_c) {
+        if (epi) {
             epilogue_any(we);
-            clear_acc();
+            clear_acc();   // here, not in each epilogue variant: one copy of the clears
         }
         // Group 0 loads its half of B chunk s+1 (ws) into the buffer of step
         // s-2, group 1 its half of chunk s+2 (wa) into that of step s-1;
@@ -774,11 +761,6 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         else
             copy_b_half(wa, bn == 2 ? 0 : bn + 1);
         copy_a32(wa, b);   // staging b held step s, split in U(s-1)
-        stores = false;
-        if (epi && !reads_c) {
-            stores = epilogue_any(we);
-            clear_acc();   // here, not in each epilogue variant: one copy of the clears
-        }
         // The first fragments of M(s) are read before the barrier where they
         // are already published: this group's A planes (split in U(s-1),
         // published by the barrier that ended M(s-1)) and B chunk s (both
@@ -826,13 +808,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         bm = bn;
         // Before the next barrier: this thread's split writes of U(s) are
         // complete (the group reads them in M(s+1)); this group's half of B
-        // loaded in U(s) has landed, while its A load of U(s) and the
-        // epilogue's stores, issued after it, may still be in flight.
+        // loaded in U(s) (and the epilogue's stores before it) has landed,
+        // while its A load of U(s), issued after it, may still be in flight.
         wait_lgkmcnt0();
-        if (stores)
-            wait_vmcnt<A_ROUNDS + EPI_STORES>();
-        else
-            wait_vmcnt<A_ROUNDS>();
+        wait_vmcnt<A_ROUNDS>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
