@@ -81,18 +81,30 @@ __device__ __forceinline__ void split_pair(float a0, float a1, uint32_t& hi, uin
     lo = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
 }
 
-// Two-piece version (hi, mid') for the three-product mode.
+// x clamped to +-bf16_sat_limit() when finite (so that R saturates), passed
+// through when +-inf or NaN (the clamp alone would make it finite).
+__device__ __forceinline__ float sat_finite(float x)
+{
+    return __builtin_fabsf(x) <= __uint_as_float(0x7F7FFFFFu) ? clamp_sat(x) : x;
+}
+
+// Two-piece version (hi, mid') for the three-product mode: the same pieces
+// as split_pair<true>, mid' saturating like hi (for |a| within 2^-15 of
+// FLT_MAX, 2^8 (a - hi) rounds past the largest BF16).  For finite a the
+// residual 2^8 (a - hi) is finite, so sat_finite only ever passes through the
+// inf/NaN of a non-finite a, which then reaches the products through mid'.
 __device__ __forceinline__ void split_pair_hm(float a0, float a1, uint32_t& hi, uint32_t& mid)
 {
     hi = pack_bf16x2(clamp_sat(a0), clamp_sat(a1));
     const float m0 = (a0 - lo_half_value(hi)) * 256.0f;
     const float m1 = (a1 - hi_half_value(hi)) * 256.0f;
-    mid = pack_bf16x2(m0, m1);
+    mid = pack_bf16x2(sat_finite(m0), sat_finite(m1));
 }
 
 // The first NP pieces of a pair (a0 in the low half of each word):
 // w[0] = hi, w[1] = mid', w[2] = lo'.  NP = 1 is the one-piece (hi only)
-// rounding of the one-product mode.
+// rounding of the one-product mode, where a non-finite a keeps its hi =
+// +-inf / NaN.
 template <int NP>
 __device__ __forceinline__ void split_pieces(float a0, float a1, uint32_t (&w)[NP])
 {
@@ -102,7 +114,7 @@ __device__ __forceinline__ void split_pieces(float a0, float a1, uint32_t (&w)[N
     else if constexpr (NP == 2)
         split_pair_hm(a0, a1, w[0], w[1]);
     else
-        w[0] = pack_bf16x2(clamp_sat(a0), clamp_sat(a1));
+        w[0] = pack_bf16x2(sat_finite(a0), sat_finite(a1));
 }
 
 }  // namespace emu

@@ -117,10 +117,9 @@ typedef enum {
  * A or B overlapping C is undefined behaviour (not checked).  Any alignment
  * and any leading dimension meeting the bounds above is accepted; 16-byte
  * aligned pointers with leading dimensions that are multiples of 4 take the
- * vectorised load path.  Non-finite inputs give non-finite outputs in
- * NATIVE_F32, BF16X9 and BF16X6 (a NaN may appear where IEEE gives +-inf);
- * BF16X3 propagates them too, but may overflow for finite inputs within
- * 2^-15 of FLT_MAX.
+ * vectorised load path.  Non-finite inputs give non-finite outputs in every
+ * mode (a NaN may appear where IEEE gives +-inf).  Finite inputs up to
+ * FLT_MAX split into finite pieces in every mode (R saturates).
  *
  * Errors: EMU_STATUS_INVALID_VALUE for M, N or K < 0, a leading dimension
  * below its bound, a NULL A or B with M*N*K > 0, a NULL C with M*N > 0, or a

@@ -120,3 +120,33 @@ def test_full_size_mlip_stack_bitwise_sampled(gi):
     del c
     _same(out, oracle.emu_gemm_mfma(a[rows], b, "BF16X9", trans_b=g.trans_b),
           f"workload 3 {g.name} rows {rows.size}")
+
+
+@pytest.mark.parametrize("mode", EMU_MODES)
+def test_operands_near_flt_max_bitwise(mode):
+    """Finite operands within 2^-15 of FLT_MAX (|x| >= 0x7F7F8000, where R
+    rounds to infinity unless it saturates), paired with small values of the
+    other operand so that every product and sum is finite: the pieces
+    saturate (hi = mid' = 0x7F7F for the largest), the result is finite,
+    equal to the model bit for bit and within the FP64 bound.  Both operands
+    in turn carry the large values (A through the fused split, and through
+    the pre-split path when transposed; B through its pre-split)."""
+    from gpu_helpers import check_result
+
+    rng = np.random.default_rng(23)
+    M, N, K = 96, 80, 72
+    big_bits = rng.integers(0x7F7F8000, 0x7F800000, size=(M, K), dtype=np.uint64).astype(np.uint32)
+    big_bits[:, :4] = [0x7F7FFFFF, 0x7F7FFFC0, 0x7F7FFF80, 0x7F7F8000]   # mid' saturates in the first three
+    big = big_bits.view(np.float32) * rng.choice(np.float32([-1, 1]), size=(M, K))
+    small = (rng.uniform(-1, 1, (K, N)) * 2.0**-40).astype(np.float32)
+    mix = rng.standard_normal((M, K)).astype(np.float32)
+    a = np.where(rng.random((M, K)) < 0.5, big, mix).astype(np.float32)
+    a[:, :4] = big[:, :4]
+    cases = [("A large", a, small, False), ("A large, transposed", a, small, True),
+             ("B large", np.ascontiguousarray(small.T), np.ascontiguousarray(a.T), False)]
+    for label, x, y, ta in cases:
+        out = run(np.ascontiguousarray(x.T) if ta else x, y, mode, trans_a=ta)
+        model = oracle.emu_gemm_mfma(x, y, mode)
+        assert np.isfinite(model).all()
+        _same(out, model, f"near FLT_MAX, {label}, {mode}")
+        check_result(out, oracle.gemm_f64(x, y), x, y, mode, label=f"near FLT_MAX {label}")

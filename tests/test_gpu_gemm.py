@@ -321,7 +321,7 @@ def test_nonfinite_inputs_propagate():
     b = np.random.default_rng(3).standard_normal((64, 64)).astype(np.float32)
     a[3, 5] = np.nan
     a[10, 7] = np.inf
-    for mode in MODES:
+    for mode in MODES + ("BF16X1",):
         say(f"non-finite {mode}")
         out = run(a, b, mode)
         assert not np.isfinite(out[3]).any() and not np.isfinite(out[10]).any(), mode
@@ -345,9 +345,11 @@ def test_inf_in_first_column_ragged_k():
     """Inf in column 0 of A with K not a multiple of 32: k past K must add
     exact zeros (the direct-load paths fill that part of the last k-step from
     column 0 and then zero it).  NATIVE_F32: the row is exactly the FP64
-    result, +-Inf (B[0, j] != 0), not NaN.  The emulated modes split Inf into
-    (Inf, 0, 0), whose products with B's pieces give Inf or NaN: there the
-    row must be non-finite and the others finite."""
+    result, +-Inf (B[0, j] != 0), not NaN.  The emulated modes' fused split
+    gives Inf a finite hi (0x7F7F) and carries the Inf in a lower piece
+    (lo' in BF16X9 and X6, mid' in BF16X3; BF16X1 keeps hi = Inf), whose
+    products with B's pieces give Inf or NaN: there the row must be
+    non-finite and the others finite."""
     rng = np.random.default_rng(12)
     for K in (36, 100, 260):
         a = rng.standard_normal((130, K)).astype(np.float32)
@@ -356,7 +358,7 @@ def test_inf_in_first_column_ragged_k():
         a[128, 0] = -np.inf
         with np.errstate(invalid="ignore", over="ignore"):
             ref = oracle.gemm_f64(a, b)
-        for mode in MODES:
+        for mode in MODES + ("BF16X1",):
             say(f"inf column 0 K={K} {mode}")
             out = run(a, b, mode)
             for r in (7, 128):

@@ -6,12 +6,11 @@ Performance for Machine Learning Interatomic Potentials", section "How Tensor
 Core FP32 bridges the hardware gap"); the GEMM kernels stage their operands
 with the same device routine, so this also checks the fused split.
 """
-import os
-
 import numpy as np
 import pytest
 
 import oracle
+import split_check
 import synth
 from gpu_helpers import say
 
@@ -77,10 +76,35 @@ def test_split_ragged_and_unaligned(n, offset):
 
 
 def test_split_sweep_of_bit_patterns():
-    """1 in 16 of all 2^32 patterns (every pattern with EMU_EXHAUSTIVE=1)."""
-    step = 1 if os.environ.get("EMU_EXHAUSTIVE") == "1" else 16
+    """Every one of the 2^32 FP32 bit patterns, in chunks of 2^26 made on the
+    device: the GPU split equals the oracle's bit for bit, and its pieces pass
+    the C range checker (exact reconstruction hi + 2^-8 mid' + 2^-16 lo' == a
+    in float64, finite pieces, piece bounds, non-finite conventions).  Stops
+    at the first failing chunk."""
+    import torch
+
+    import emulated_fp32_matrix_amd as emu
+
+    dev = torch.device("cuda:0")
     chunk = 2**26
-    total = 2**32 // step
-    for c0 in range(0, total, chunk):
-        idx = np.arange(c0, min(c0 + chunk, total), dtype=np.uint64) * step + (c0 // chunk) % step
-        _check(idx.astype(np.uint32).view(np.float32), label=f"sweep chunk {c0 // chunk}")
+    planes = [torch.empty(chunk, dtype=torch.int16, device=dev) for _ in range(3)]
+    stream = torch.cuda.current_stream().cuda_stream
+    for c in range(2**32 // chunk):
+        first = c * chunk
+        bits = torch.arange(first, first + chunk, dtype=torch.int64, device=dev)
+        bits = torch.where(bits >= 2**31, bits - 2**32, bits).to(torch.int32)
+        x = bits.view(torch.float32)
+        st = emu.emu_split_bf16x3(x.data_ptr(), chunk, *(p.data_ptr() for p in planes), stream)
+        assert st == emu.STATUS_SUCCESS, emu.emu_status_string(st)
+        got = [p.cpu().numpy().view(np.uint16) for p in planes]   # synchronises
+        u = np.arange(first, first + chunk, dtype=np.uint64).astype(np.uint32)
+        want = oracle.split_bf16x3(u.view(np.float32))
+        for name, g, w in zip(("hi", "mid", "lo"), got, want):
+            bad = np.nonzero(g != w)[0]
+            assert bad.size == 0, (f"chunk {c} {name}: {bad.size} mismatches, first at bits "
+                                   f"{hex(first + int(bad[0]))}: gpu {hex(int(g[bad[0]]))} "
+                                   f"oracle {hex(int(w[bad[0]]))}")
+        nbad, at = split_check.check_range(first, *got)
+        assert nbad == 0, f"chunk {c}: {nbad} pieces fail the checker, first at bits {hex(first + at)}"
+        if c % 8 == 7:
+            say(f"split sweep: {c + 1} of {2**32 // chunk} chunks of 2^26 bit-exact")

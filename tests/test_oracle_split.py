@@ -8,21 +8,19 @@ round-to-nearest-even, saturating.  The page prints no worked example, so the
 oracle is pinned to what the mathematics fixes:
 
 * exact reconstruction a == hi + 2^-8 mid' + 2^-16 lo' (checked in float64,
-  independently of the oracle's code) over a dense sweep of bit patterns,
-  and over all 2^32 patterns with EMU_EXHAUSTIVE=1;
+  independently of the oracle's code) over dense sweeps of bit patterns, and
+  over all 2^32 patterns (the C range checker of split_check.c);
 * the nearest-piece bounds |2^-8 mid'| <= ulp(hi)/2, |2^-16 lo'| <= ulp(2^-8 mid')/2;
 * R itself against torch's FP32 -> BF16 conversion (a library routine, round
   to nearest even) wherever no saturation occurs;
 * hand-derived special cases (below, each with its derivation);
 * sign symmetry and the non-finite conventions.
 """
-import os
-
 import numpy as np
-import pytest
 import torch
 
 import oracle
+import split_check
 
 F32_TOP = 0x7F7F8000  # |a| >= this rounds to BF16 infinity without saturation
 
@@ -171,11 +169,35 @@ def test_reconstruction_strided_sweep():
     check_split_invariants(_from_bits(u))
 
 
-@pytest.mark.slow
-@pytest.mark.skipif(os.environ.get("EMU_EXHAUSTIVE") != "1", reason="set EMU_EXHAUSTIVE=1")
+def test_checker_catches_wrong_pieces():
+    """The range checker used by the exhaustive sweeps flags pieces that miss
+    by one unit in any plane, a piece outside its bound, and wrong
+    non-finite conventions."""
+    u = np.arange(0x3F800000, 0x3F800000 + 4096, dtype=np.uint32)
+    hi, mid, lo = oracle.split_bf16x3(_from_bits(u))
+    assert split_check.check_range(0x3F800000, hi, mid, lo) == (0, -1)
+    for plane in range(3):
+        bad = [p.copy() for p in (hi, mid, lo)]
+        bad[plane][100] ^= 1
+        assert split_check.check_range(0x3F800000, *bad) == (1, 100), plane
+    # a = 1 + 2^-8 + 2^-16: (1, 2^-8 + 2^-15, -2^-16) also reconstructs a, but
+    # its hi is not the nearest BF16 (|2^-8 mid'| > ulp(1)/2 = 2^-8); the
+    # split is (1 + 2^-7, -(2^-8 - 2^-16), 0)
+    assert split_check.check_range(0x3F808080, [0x3F80], [0x3F81], [0xBF80]) == (1, 0)
+    assert split_check.check_range(0x3F808080, [0x3F81], [0xBF7F], [0]) == (0, -1)
+    assert split_check.check_range(0x7F800000, [0x7F7F], [0x7F7F], [0x7F80]) == (1, 0)
+    assert split_check.check_range(0x7FC00000, [0x7FC0], [0], [0]) == (0, -1)
+
+
 def test_reconstruction_exhaustive():
-    """All 2^32 bit patterns, in chunks of 2^24."""
-    step = 2**24
+    """All 2^32 bit patterns, in chunks of 2^26, through the C range checker
+    (reconstruction in float64, finite pieces, piece bounds, non-finite
+    conventions); stops at the first failing chunk."""
+    step = 2**26
     for c in range(2**32 // step):
-        u = np.arange(c * step, (c + 1) * step, dtype=np.uint64).astype(np.uint32)
-        check_split_invariants(_from_bits(u))
+        first = c * step
+        u = np.arange(first, first + step, dtype=np.uint64).astype(np.uint32)
+        hi, mid, lo = oracle.split_bf16x3(_from_bits(u))
+        bad, at = split_check.check_range(first, hi, mid, lo)
+        assert bad == 0, (f"chunk {c}: {bad} failures, first at bits {hex(first + at)}: "
+                          f"{hex(int(hi[at]))} {hex(int(mid[at]))} {hex(int(lo[at]))}")
