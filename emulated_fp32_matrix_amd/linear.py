@@ -15,6 +15,11 @@ in_features]):
   backward  dx = dy W        emu_sgemm (transB = N);
             dW = dy^T x      torch FP32 matmul (TF32 off), db = sum of dy rows.
 
+The backward is itself differentiable (create_graph=True), as training on
+forces needs: dx = dy W is an autograd function whose own gradients are
+again an emulated product (for dy) and an FP32 weight-gradient product (for
+W), and dW, db are torch operations.
+
 The mode ("AUTO" = the performant policy, "BF16X9" = eager, "BF16X6",
 "BF16X3", "NATIVE_F32") applies to both library GEMMs.
 
@@ -76,6 +81,53 @@ def _as_rows(t, width):
     return t2 if t2.is_contiguous() else t2.contiguous()
 
 
+def _fp32_matmul(a, b):
+    """a @ b in torch FP32 with TF32 off: the weight-gradient products, which
+    stay in ordinary precision."""
+    prev = torch.backends.cuda.matmul.allow_tf32
+    torch.backends.cuda.matmul.allow_tf32 = False
+    try:
+        return a.matmul(b)
+    finally:
+        torch.backends.cuda.matmul.allow_tf32 = prev
+
+
+def _cache_for(caches, trans_w):
+    # caches = (planes of W^T, planes of W)
+    return None if not caches else caches[0 if trans_w else 1]
+
+
+class _EmuMatmulFunction(torch.autograd.Function):
+    """y = a @ op(w), op(w) = w^T (trans_w) or w, through the library: the
+    layer's input-gradient product dx = dy W, differentiable again, so that
+    a loss on forces (a first derivative of the energy) can be
+    differentiated once more (create_graph=True).  Its gradients:
+    d/da = g @ op(w)^T, again this emulated product; d/dw = g^T a (trans_w)
+    or a^T g, a weight-gradient product in torch FP32."""
+
+    @staticmethod
+    def forward(ctx, a, w, trans_w, mode, caches):
+        a2 = a if a.is_contiguous() else a.contiguous()
+        wc = w if w.is_contiguous() else w.contiguous()
+        y = _gemm(a2, wc, trans_w, mode, None, _cache_for(caches, trans_w) if wc is w else None)
+        ctx.save_for_backward(a, w)
+        ctx.trans_w = trans_w
+        ctx.mode = mode
+        ctx.caches = caches
+        return y
+
+    @staticmethod
+    def backward(ctx, g):
+        a, w = ctx.saved_tensors
+        g2 = g if g.is_contiguous() else g.contiguous()
+        ga = gw = None
+        if ctx.needs_input_grad[0]:
+            ga = _EmuMatmulFunction.apply(g2, w, not ctx.trans_w, ctx.mode, ctx.caches)
+        if ctx.needs_input_grad[1]:
+            gw = _fp32_matmul(g2.t(), a) if ctx.trans_w else _fp32_matmul(a.t(), g2)
+        return ga, gw, None, None, None
+
+
 class _EmuLinearFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, weight, bias, mode, caches):
@@ -85,29 +137,25 @@ class _EmuLinearFunction(torch.autograd.Function):
         x2 = _as_rows(x, in_f)
         w = weight if weight.is_contiguous() else weight.contiguous()
         y = _gemm(x2, w, True, mode, bias, caches[0] if caches and w is weight else None)
-        ctx.save_for_backward(x2, w)
+        # the inputs themselves are saved, so that the products formed from
+        # them in backward stay connected to the graph (double backward)
+        ctx.save_for_backward(x, weight)
         ctx.has_bias = bias is not None
         ctx.mode = mode
-        ctx.caches = caches if w is weight else None
-        ctx.x_shape = x.shape
+        ctx.caches = caches
         return y.reshape(*x.shape[:-1], out_f)
 
     @staticmethod
     def backward(ctx, gy):
-        x2, w = ctx.saved_tensors
-        out_f, in_f = w.shape
+        x, weight = ctx.saved_tensors
+        out_f, in_f = weight.shape
         gy2 = _as_rows(gy, out_f)
         gx = gw = gb = None
         if ctx.needs_input_grad[0]:
-            gx = _gemm(gy2, w, False, ctx.mode, None,
-                       ctx.caches[1] if ctx.caches else None).reshape(ctx.x_shape)
+            # dx = dy W: emulated, and differentiable (force training)
+            gx = _EmuMatmulFunction.apply(gy2, weight, False, ctx.mode, ctx.caches).reshape(x.shape)
         if ctx.needs_input_grad[1]:
-            prev = torch.backends.cuda.matmul.allow_tf32
-            torch.backends.cuda.matmul.allow_tf32 = False
-            try:
-                gw = gy2.t().matmul(x2)
-            finally:
-                torch.backends.cuda.matmul.allow_tf32 = prev
+            gw = _fp32_matmul(gy2.t(), _as_rows(x, in_f))
         if ctx.has_bias and ctx.needs_input_grad[2]:
             gb = gy2.sum(dim=0)
         return gx, gw, gb, None, None

@@ -232,3 +232,38 @@ def test_emulinear_cached_weights_bitwise(mode):
             cached.weight.add_(1.0)
             cached(torch.randn(64, 256, device="cuda"))
             assert cached._caches[0].planes is not first   # in-place update: split again
+
+
+@pytest.mark.parametrize("mode", ["BF16X9", "AUTO", "NATIVE_F32"])
+@pytest.mark.parametrize("cache_weights", [False, True])
+def test_emulinear_force_loss_double_backward(mode, cache_weights):
+    """Training on forces: E = sum(l2(tanh(l1(x)))), F = -dE/dx with
+    create_graph=True (the input-gradient GEMM through the library), then
+    L = |F|^2 differentiated again.  Every gradient of L (both layers'
+    weights, the first bias, x) is compared with torch float64 on the CPU;
+    the second-order terms run through the library's emulated products."""
+    import torch
+
+    from emulated_fp32_matrix_amd.linear import EmuLinear
+
+    torch.manual_seed(7)
+    l1 = EmuLinear(256, 512, mode=mode, device="cuda:0", cache_weights=cache_weights)
+    l2 = EmuLinear(512, 64, mode=mode, device="cuda:0", cache_weights=cache_weights)
+    x = torch.randn(3000, 256, device="cuda:0", requires_grad=True)
+
+    def loss_of(f1, f2, xx):
+        e = f2(torch.tanh(f1(xx))).sum()
+        (gx,) = torch.autograd.grad(e, xx, create_graph=True)
+        return ((-gx) ** 2).sum()
+
+    params = [l1.weight, l1.bias, l2.weight]
+    got = torch.autograd.grad(loss_of(l1, l2, x), params + [x])
+    p64 = [p.detach().cpu().double().requires_grad_(True) for p in (l1.weight, l1.bias, l2.weight, l2.bias)]
+    x64 = x.detach().cpu().double().requires_grad_(True)
+    want = torch.autograd.grad(
+        loss_of(lambda t: torch.nn.functional.linear(t, p64[0], p64[1]),
+                lambda t: torch.nn.functional.linear(t, p64[2], p64[3]), x64), p64[:3] + [x64])
+    for name, g, w in zip(("W1", "b1", "W2", "x"), got, want):
+        rel = _rel(g, w)
+        say(f"force loss {mode} cache={cache_weights}: dL/d{name} rel err {rel:.2e}")
+        assert rel <= 1e-5, (name, rel)
