@@ -8,7 +8,7 @@ this package fails if the library has not been built, and every call raises
 
 Low-level entry points mirror the C ABI one to one (pointers are ints):
 :func:`emu_sgemm`, :func:`emu_sgemm_bias`, :func:`emu_sgemm_ex`,
-:func:`emu_split_bf16x3`, :func:`emu_sgemm_select`, :func:`emu_sgemm_ksplit`,
+:func:`emu_sgemm_noalloc`, :func:`emu_split_bf16x3`, :func:`emu_sgemm_select`, :func:`emu_sgemm_ksplit`,
 :func:`emu_status_string`, :func:`emu_abi_version`.  :func:`sgemm` and
 :func:`split_bf16x3` accept torch tensors.
 
@@ -31,11 +31,15 @@ STATUS_SUCCESS = 0
 STATUS_INVALID_VALUE = 1
 STATUS_NOT_SUPPORTED = 2
 STATUS_LAUNCH_FAILED = 3
+STATUS_ALLOC_FAILED = 4
+STATUS_INTERNAL = 5
+STATUS_SCRATCH_TOO_SMALL = 6
+NOALLOC_SCRATCH_BYTES = 64 << 20   # EMU_NOALLOC_SCRATCH_BYTES
 
 # C functions declared in include/emu_sgemm.h
 EXPORTS = ("emu_sgemm", "emu_sgemm_bias", "emu_sgemm_ex", "emu_split_bf16x3", "emu_sgemm_select",
            "emu_sgemm_ksplit", "emu_presplit_b_bytes", "emu_presplit_b", "emu_sgemm_presplit",
-           "emu_status_string", "emu_abi_version")
+           "emu_sgemm_noalloc", "emu_status_string", "emu_abi_version")
 
 
 class EmuError(RuntimeError):
@@ -70,6 +74,8 @@ _lib.emu_sgemm_ex.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, ctyp
                               _i64, _vp, _i64, ctypes.c_float, _vp, _i64, _vp, ctypes.c_int,
                               ctypes.c_int, _vp]
 _lib.emu_sgemm_ex.restype = ctypes.c_int
+_lib.emu_sgemm_noalloc.argtypes = _lib.emu_sgemm_ex.argtypes
+_lib.emu_sgemm_noalloc.restype = ctypes.c_int
 _lib.emu_sgemm_ksplit.argtypes = [_i64, _i64, _i64, ctypes.POINTER(ctypes.c_int)]
 _lib.emu_sgemm_ksplit.restype = ctypes.c_int
 _lib.emu_presplit_b_bytes.argtypes = [_i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
@@ -127,6 +133,15 @@ def emu_sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, b
     return int(_lib.emu_sgemm_ex(int(transA), int(transB), int(M), int(N), int(K), float(alpha),
                                  A or None, int(lda), B or None, int(ldb), float(beta), C or None,
                                  int(ldc), bias or None, _mode(mode), int(ksplit), stream or None))
+
+
+def emu_sgemm_noalloc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, mode,
+                      ksplit, stream) -> int:
+    """Raw call of the allocation-free variant of emu_sgemm_ex; returns the
+    status code (pointers and stream are ints)."""
+    return int(_lib.emu_sgemm_noalloc(int(transA), int(transB), int(M), int(N), int(K), float(alpha),
+                                      A or None, int(lda), B or None, int(ldb), float(beta), C or None,
+                                      int(ldc), bias or None, _mode(mode), int(ksplit), stream or None))
 
 
 def emu_sgemm_ksplit(M, N, K):

@@ -36,10 +36,24 @@ struct DeviceSlot {
     emu::DeviceInfo info{};
     WsEntry ws[kWsEntries];
     uint64_t tick = 0;
+    bool pool_tried = false;       // the workspace pool is made on first use
+    void* scratch = nullptr;       // this device's copy of `scratch` (null: unresolved)
 };
 
 std::mutex g_dev_mutex;
 DeviceSlot g_dev[kMaxDevices];
+
+// The workspace of emu_sgemm_noalloc: device memory that is part of the
+// library's code object, so a call never allocates.  Each device holds its
+// own copy, from the library's first use on that device until the process
+// ends.  In host code `scratch` is only a stand-in for the symbol: its
+// device address, per device, comes from hipGetSymbolAddress when the
+// device is first used (current_device) and is what the kernels receive.
+// Calls on one device share the copy, so emu_sgemm_noalloc calls that
+// overlap on a device race; no kernel needs it zeroed (every byte a kernel
+// reads, it or an earlier kernel of the same call wrote).
+constexpr size_t kScratchBytes = (size_t)EMU_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 // A memory pool on device `dev` that keeps up to kPoolKeepBytes of freed
 // memory mapped; null (and no error left behind) if one cannot be made.
@@ -77,11 +91,18 @@ bool current_device(emu::DeviceInfo& info)
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
         s.supported = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
         s.info.num_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
-        // A pool of our own for the stream workspaces (keeping freed memory
-        // mapped up to kPoolKeepBytes); without it the device's default pool
-        // is used.
         s.info.device = dev;
-        s.info.pool = s.supported ? make_pool(dev) : nullptr;
+        s.info.pool = nullptr;
+        if (s.supported) {
+            // this device's copy of the no-allocation scratch (the device is current)
+            void* ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr != nullptr) {
+                s.scratch = ptr;
+            } else {
+                s.scratch = nullptr;
+                (void)hipGetLastError();   // reported by emu_sgemm_noalloc, not by a later launch
+            }
+        }
         s.ready = true;
     }
     info = s.info;
@@ -101,6 +122,14 @@ hipError_t stream_workspace(const emu::DeviceInfo& info, hipStream_t st, size_t 
 {
     std::lock_guard<std::mutex> lock(g_dev_mutex);
     DeviceSlot& d = g_dev[info.device];
+    if (!d.pool_tried) {
+        // A pool of our own for the stream workspaces (keeping freed memory
+        // mapped up to kPoolKeepBytes); without it the device's default pool
+        // is used.
+        d.info.pool = make_pool(info.device);
+        d.pool_tried = true;
+    }
+    const hipMemPool_t pool = d.info.pool;
     ++d.tick;
     WsEntry* e = nullptr;
     for (WsEntry& w : d.ws)
@@ -129,8 +158,8 @@ hipError_t stream_workspace(const emu::DeviceInfo& info, hipStream_t st, size_t 
             e->size = 0;
         }
         void* p = nullptr;
-        const hipError_t r = info.pool != nullptr ? hipMallocFromPoolAsync(&p, want, info.pool, st)
-                                                  : hipMallocAsync(&p, want, st);
+        const hipError_t r = pool != nullptr ? hipMallocFromPoolAsync(&p, want, pool, st)
+                                             : hipMallocAsync(&p, want, st);
         if (r != hipSuccess) {
             (void)hipGetLastError();   // reported as EMU_STATUS_ALLOC_FAILED, not by a later launch
             return hipErrorOutOfMemory;
@@ -140,6 +169,14 @@ hipError_t stream_workspace(const emu::DeviceInfo& info, hipStream_t st, size_t 
     }
     *out = e->ptr;
     return hipSuccess;
+}
+
+// The device address of `scratch` on device `dev`, resolved by
+// current_device() (null if that failed).
+void* device_scratch(int dev)
+{
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    return g_dev[dev].scratch;
 }
 
 bool valid_op(int op) { return op == EMU_OP_N || op == EMU_OP_T; }
@@ -240,10 +277,12 @@ namespace {
 
 // planes: op(B) pre-split by emu_presplit_b (then B, ldb and transB are not
 // used and mode must be an emulated one), or null.
+// noalloc: the workspace is this device's scratch (EMU_STATUS_SCRATCH_TOO_SMALL
+// when the call needs more), never the stream's allocated buffer.
 emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
                         float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
                         float beta, float* C, int64_t ldc, const float* bias, emu_mode_t mode,
-                        int ksplit, void* stream, const void* planes = nullptr)
+                        int ksplit, void* stream, const void* planes = nullptr, bool noalloc = false)
 {
     // ---- validation: no HIP call before this block has passed ----
     if (!valid_op(transA) || !valid_op(transB)) return EMU_STATUS_INVALID_VALUE;
@@ -265,6 +304,18 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     emu::DeviceInfo dev;
     if (!current_device(dev)) return EMU_STATUS_NOT_SUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    void* const scratch_ptr = noalloc ? device_scratch(dev.device) : nullptr;
+    if (noalloc && scratch_ptr == nullptr) return EMU_STATUS_INTERNAL;
+    // the call's workspace: the stream's buffer, or the scratch
+    auto workspace = [&](size_t bytes, void** ws) -> emu_status_t {
+        if (noalloc) {
+            if (bytes > kScratchBytes) return EMU_STATUS_SCRATCH_TOO_SMALL;
+            *ws = scratch_ptr;
+            return EMU_STATUS_SUCCESS;
+        }
+        return stream_workspace(dev, s, bytes, ws) == hipSuccess ? EMU_STATUS_SUCCESS
+                                                                 : EMU_STATUS_ALLOC_FAILED;
+    };
 
     if (K == 0 || alpha == 0.0f) return from_hip(emu::launch_scale_c(M, N, beta, C, ldc, bias, s));
 
@@ -289,8 +340,10 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     if (mode == EMU_MODE_NATIVE_F32) {
         void* ws = nullptr;
         const size_t ws_bytes = emu::gemm_native_f32_workspace_bytes(g);
-        if (ws_bytes > 0 && stream_workspace(dev, s, ws_bytes, &ws) != hipSuccess)
-            return EMU_STATUS_ALLOC_FAILED;
+        if (ws_bytes > 0) {
+            const emu_status_t st = workspace(ws_bytes, &ws);
+            if (st != EMU_STATUS_SUCCESS) return st;
+        }
         return from_hip(emu::launch_gemm_native_f32(g, dev, ws, s));
     }
     const bool fused = emu::fused_a_path(g);
@@ -309,8 +362,10 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     }
     void* ws = nullptr;
     const size_t ws_bytes = emu::gemm_bf16_workspace_bytes(g, nbands, ksplit);
-    if (ws_bytes > 0 && stream_workspace(dev, s, ws_bytes, &ws) != hipSuccess)
-        return EMU_STATUS_ALLOC_FAILED;
+    if (ws_bytes > 0) {
+        const emu_status_t st = workspace(ws_bytes, &ws);
+        if (st != EMU_STATUS_SUCCESS) return st;
+    }
     return from_hip(emu::launch_gemm_bf16(g, nbands, ksplit, dev, ws, s));
 }
 
@@ -339,11 +394,12 @@ const char* emu_status_string(emu_status_t status)
     case EMU_STATUS_LAUNCH_FAILED: return "EMU_STATUS_LAUNCH_FAILED";
     case EMU_STATUS_ALLOC_FAILED: return "EMU_STATUS_ALLOC_FAILED";
     case EMU_STATUS_INTERNAL: return "EMU_STATUS_INTERNAL";
+    case EMU_STATUS_SCRATCH_TOO_SMALL: return "EMU_STATUS_SCRATCH_TOO_SMALL";
     default: return "EMU_STATUS_UNKNOWN";
     }
 }
 
-int emu_abi_version(void) { return 105; }
+int emu_abi_version(void) { return 106; }
 
 emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
                               emu_mode_t* chosen)
@@ -409,6 +465,15 @@ emu_status_t emu_sgemm_presplit(emu_op_t transA, int64_t M, int64_t N, int64_t K
     // (B and ldb are not read; ldb = max(1, N) passes the op(B) check)
     return sgemm_impl(transA, EMU_OP_N, M, N, K, alpha, A, lda, nullptr, max1(N), beta, C, ldc, bias,
                       mode, ksplit, stream, planes);
+}
+
+emu_status_t emu_sgemm_noalloc(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
+                               float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                               float beta, float* C, int64_t ldc, const float* bias, emu_mode_t mode,
+                               int ksplit, void* stream)
+{
+    return sgemm_impl(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, mode,
+                      ksplit, stream, nullptr, true);
 }
 
 emu_status_t emu_sgemm_ksplit(int64_t M, int64_t N, int64_t K, int* ksplit)

@@ -43,7 +43,8 @@
  *     the stream.  Up to 16 streams per device keep a buffer; beyond that the
  *     least recently used one is released with hipFree, which waits for the
  *     device.  The buffers live until the process ends.  emu_split_bf16x3
- *     allocates nothing.  The cache knows streams only by their handle:
+ *     allocates nothing, and emu_sgemm_noalloc works in a fixed scratch
+ *     instead of a stream's buffer.  The cache knows streams only by their handle:
  *     synchronise a stream that ran library calls before destroying it, so
  *     that a new stream that receives the same handle cannot overlap its
  *     work with the old stream's in the shared buffer.
@@ -91,8 +92,15 @@ typedef enum {
     EMU_STATUS_NOT_SUPPORTED = 2,  /* no gfx950 device current, or device query failed */
     EMU_STATUS_LAUNCH_FAILED = 3,  /* the kernel launch itself reported an error */
     EMU_STATUS_ALLOC_FAILED = 4,   /* the stream's workspace could not be allocated or grown */
-    EMU_STATUS_INTERNAL = 5
+    EMU_STATUS_INTERNAL = 5,
+    /* emu_sgemm_noalloc: the call needs more workspace than the library's
+     * fixed scratch holds (EMU_NOALLOC_SCRATCH_BYTES); nothing was launched.
+     * (ABI 1.6) */
+    EMU_STATUS_SCRATCH_TOO_SMALL = 6
 } emu_status_t;
+
+/* Bytes of the fixed per-device scratch emu_sgemm_noalloc works in. */
+#define EMU_NOALLOC_SCRATCH_BYTES (64ull << 20)
 
 /*
  * C = alpha * op(A) . op(B) + beta * C in FP32, computed in `mode`.
@@ -189,6 +197,37 @@ emu_status_t emu_sgemm_ex(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N
                           int ksplit, void* stream);
 
 /*
+ * emu_sgemm_ex that never allocates, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Arguments, modes, results (bit for bit), asynchrony
+ * and errors are those of emu_sgemm_ex.  The only difference is the
+ * workspace (the BF16 planes of op(B), of op(A) when A is not split inside
+ * the GEMM, the partial results of a split K, or NATIVE_F32's packed
+ * op(B); sizes in the Memory paragraph at the top of this file): instead of
+ * the stream's allocated buffer, the call uses a scratch of
+ * EMU_NOALLOC_SCRATCH_BYTES (64 MiB) that is part of the library's device
+ * code object.  Each device holds its own copy from the library's first use
+ * on that device (its address is resolved then, once per device) until the
+ * process ends.  A call allocates nothing: no hipMalloc, no hipFree, no
+ * memory pool, no library routine that allocates.
+ *
+ * Every call on a device shares that device's scratch, and the scratch
+ * keeps the last call's contents (no call needs it cleared).  Calls that
+ * overlap on one device race: issue them on one stream, or order them.
+ * A graph that captures calls on several streams must order those calls.
+ *
+ * Errors: as emu_sgemm_ex; also EMU_STATUS_SCRATCH_TOO_SMALL, before any
+ * launch, when the call needs more than EMU_NOALLOC_SCRATCH_BYTES (for
+ * example a split K of S * M * N * 4 bytes beyond it), and
+ * EMU_STATUS_INTERNAL if the scratch's address could not be resolved.
+ * (ABI 1.6)
+ */
+emu_status_t emu_sgemm_noalloc(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
+                               float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                               float beta, float* C, int64_t ldc, const float* bias, emu_mode_t mode,
+                               int ksplit, void* stream);
+
+/*
  * The K split EMU_MODE_AUTO uses for this shape when it runs the emulation and
  * A allows a split (see emu_sgemm_ex); a caller of an explicit emulated mode
  * may pass it to emu_sgemm_ex.  It is the divisor S <= 8 of ceil(K / 32)
@@ -277,11 +316,12 @@ emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64
  * codes give "EMU_STATUS_UNKNOWN".  Never NULL. */
 const char* emu_status_string(emu_status_t status);
 
-/* ABI version of this header (major * 100 + minor): 105 (1.1 added
+/* ABI version of this header (major * 100 + minor): 106 (1.1 added
  * emu_sgemm_bias, 1.2 EMU_MODE_BF16X1, 1.3 emu_sgemm_ex and
  * emu_sgemm_ksplit, 1.4 emu_presplit_b_bytes, emu_presplit_b and
  * emu_sgemm_presplit, 1.5 a stream workspace for NATIVE_F32, which may
- * therefore return EMU_STATUS_ALLOC_FAILED). */
+ * therefore return EMU_STATUS_ALLOC_FAILED, 1.6 emu_sgemm_noalloc and
+ * EMU_STATUS_SCRATCH_TOO_SMALL). */
 int emu_abi_version(void);
 
 #ifdef __cplusplus

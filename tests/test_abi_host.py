@@ -44,8 +44,17 @@ def test_status_strings_and_version():
     assert emu.emu_status_string(1) == "EMU_STATUS_INVALID_VALUE"
     assert emu.emu_status_string(2) == "EMU_STATUS_NOT_SUPPORTED"
     assert emu.emu_status_string(3) == "EMU_STATUS_LAUNCH_FAILED"
+    assert emu.emu_status_string(4) == "EMU_STATUS_ALLOC_FAILED"
+    assert emu.emu_status_string(5) == "EMU_STATUS_INTERNAL"
+    assert emu.emu_status_string(6) == "EMU_STATUS_SCRATCH_TOO_SMALL"
     assert emu.emu_status_string(99) == "EMU_STATUS_UNKNOWN"
-    assert emu.emu_abi_version() == 105
+    assert emu.emu_abi_version() == 106
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define EMU_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == emu.NOALLOC_SCRATCH_BYTES
 
 
 FAKE = 0x1000  # never dereferenced: validation fails (or returns) before any HIP call
@@ -101,11 +110,12 @@ def test_bias_entry_point_invalid_arguments_rejected(args):
     dict(ksplit=2, K=0, lda=1, ldb=6),   # nothing to split
     dict(transA=2), dict(mode=6), dict(M=-1), dict(lda=7), dict(C=0),
 ])
-def test_split_entry_point_invalid_arguments_rejected(args):
+@pytest.mark.parametrize("fn", ["emu_sgemm_ex", "emu_sgemm_noalloc"])
+def test_split_entry_point_invalid_arguments_rejected(args, fn):
     call = dict(transA=0, transB=0, M=10, N=6, K=64, alpha=1.0, A=FAKE, lda=64, B=FAKE, ldb=6,
                 beta=0.0, C=FAKE, ldc=6, bias=0, mode=1, ksplit=2, stream=0)
     call.update(args)
-    assert emu.emu_sgemm_ex(**call) == emu.STATUS_INVALID_VALUE
+    assert getattr(emu, fn)(**call) == emu.STATUS_INVALID_VALUE
 
 
 def test_presplit_sizes():
@@ -180,6 +190,8 @@ def test_empty_shapes_return_before_touching_the_device():
     assert emu.emu_sgemm(M=0, N=5, K=4, lda=4, ldb=5, ldc=5, **base) == emu.STATUS_SUCCESS
     assert emu.emu_sgemm(M=5, N=0, K=4, lda=4, ldb=1, ldc=1, **base) == emu.STATUS_SUCCESS
     assert emu.emu_sgemm_bias(M=0, N=5, K=4, lda=4, ldb=5, ldc=5, bias=0, **base) == \
+        emu.STATUS_SUCCESS
+    assert emu.emu_sgemm_noalloc(M=0, N=5, K=4, lda=4, ldb=5, ldc=5, bias=0, ksplit=0, **base) == \
         emu.STATUS_SUCCESS
     assert emu.emu_split_bf16x3(0, 0, 0, 0, 0, 0) == emu.STATUS_SUCCESS
 
