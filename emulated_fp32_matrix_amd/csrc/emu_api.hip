@@ -208,33 +208,52 @@ constexpr double kCUs = 256.0;
 constexpr double kRedFixed = 4.0;        // us: reduction launch and tail
 constexpr double kRedBytesPerUs = 4.0e6; // bytes per us moved by the reduction
 constexpr int kMaxSplit = 8;
+// The emulated kernel's output tiles have 128 or 64 rows (fused-A path).  A
+// k-step of a 64-row tile does half the MFMAs and splits half the A rows of
+// a 128-row one but copies the same B chunk: it costs this fraction of it.
+constexpr double kX9Step64 = 0.59;
 
 double ceil_div(double a, double b) { return std::ceil(a / b); }
 
-double predict_x9_us(int64_t M, int64_t N, int64_t K, int split)
+double predict_x9_us(int64_t M, int64_t N, int64_t K, int split, int tile_m)
 {
-    const double tiles = ceil_div((double)M, 128.0) * ceil_div((double)N, 128.0);
+    const double tiles = ceil_div((double)M, (double)tile_m) * ceil_div((double)N, 128.0);
     const double nk = ceil_div((double)K, 32.0);
     const double items = tiles * split;
-    const double step = items >= kCUs ? kX9StepFull : kX9StepPart;
+    const double step = (items >= kCUs ? kX9StepFull : kX9StepPart) * (tile_m == 64 ? kX9Step64 : 1.0);
     double t = kX9Fixed + ceil_div(items, kCUs) * (nk / split) * step;
     if (split > 1) t += kRedFixed + (double)(split + 1) * (double)M * (double)N * 4.0 / kRedBytesPerUs;
     return t;
 }
 
+// The rows of the emulated kernel's output tiles for a call with `split` K
+// segments (fused-A path; the result does not depend on it): 64 where the
+// cost model predicts them at least 3 % faster than 128-row tiles (too few
+// 128-row tiles to fill the CUs, or a last round of tiles mostly idle).
+int choose_tile_m(int64_t M, int64_t N, int64_t K, int split)
+{
+    if (M == 0 || N == 0 || K == 0) return 128;
+    return predict_x9_us(M, N, K, split, 64) < 0.97 * predict_x9_us(M, N, K, split, 128) ? 64 : 128;
+}
+
+double predict_x9_best_us(int64_t M, int64_t N, int64_t K, int split)
+{
+    return predict_x9_us(M, N, K, split, choose_tile_m(M, N, K, split));
+}
+
 // The K split the emulated path uses by itself (fused-A path): the divisor
-// S <= kMaxSplit of ceil(K/32) with the least predicted time, and 1 unless
-// that saves at least 5 %.
+// S <= kMaxSplit of ceil(K/32) with the least predicted time (each with its
+// own tile choice), and 1 unless that saves at least 5 %.
 int choose_ksplit(int64_t M, int64_t N, int64_t K)
 {
     if (M == 0 || N == 0 || K == 0) return 1;
     const int64_t nk = (K + 31) / 32;
-    const double t1 = predict_x9_us(M, N, K, 1);
+    const double t1 = predict_x9_best_us(M, N, K, 1);
     int best = 1;
     double tbest = t1;
     for (int sp = 2; sp <= kMaxSplit && sp <= nk; ++sp) {
         if (nk % sp != 0) continue;
-        const double t = predict_x9_us(M, N, K, sp);
+        const double t = predict_x9_best_us(M, N, K, sp);
         if (t < tbest) {
             tbest = t;
             best = sp;
@@ -247,7 +266,7 @@ void predict_us(int64_t M, int64_t N, int64_t K, double& f32, double& x9)
 {
     const double tiles = ceil_div((double)M, 128.0) * ceil_div((double)N, 128.0);
     const double nk = ceil_div((double)K, 32.0);
-    x9 = predict_x9_us(M, N, K, choose_ksplit(M, N, K));
+    x9 = predict_x9_best_us(M, N, K, choose_ksplit(M, N, K));
     f32 = kF32Fixed + ceil_div(tiles, kCUs) * nk * (tiles >= kCUs ? kF32StepFull : kF32StepPart);
 }
 
@@ -366,7 +385,7 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
         const emu_status_t st = workspace(ws_bytes, &ws);
         if (st != EMU_STATUS_SUCCESS) return st;
     }
-    return from_hip(emu::launch_gemm_bf16(g, nbands, ksplit, dev, ws, s));
+    return from_hip(emu::launch_gemm_bf16(g, nbands, ksplit, choose_tile_m(M, N, K, ksplit), dev, ws, s));
 }
 
 // Bands of an emulated mode (0 for NATIVE_F32 and AUTO).

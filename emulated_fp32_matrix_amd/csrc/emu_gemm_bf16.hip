@@ -444,23 +444,27 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 // GENERAL: the epilogue reads C (beta != 0) or adds a bias; the plain
 // instantiation (C = alpha t) carries neither path, which saves it SGPR
 // spills and registers in the loop (1.6 % on the 552,960-row stack).
-template <int NB, bool SPLIT, bool GENERAL>
+// TH: rows of an output tile, 128 or 64 (the 64-row tiles give shapes with
+// few tiles more of them; each group then owns 32 rows).
+template <int NB, bool SPLIT, bool GENERAL, int TH>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const uint16_t* __restrict__ Wb)
 {
     static_assert(!(SPLIT && GENERAL), "a split K adds beta C and the bias in the reduction");
+    static_assert(TH == 128 || TH == 64, "output tiles of 128 or 64 rows");
     constexpr int NP = NB >= 3 ? 3 : NB;
     constexpr int CHUNK_BYTES = (int)chunk_elems(NP) * 2;
     constexpr int GT = 256;                                // threads per group
-    constexpr int GROWS = TILE / 2;                        // A rows per group
+    constexpr int GROWS = TH / 2;                          // A rows per group
+    constexpr int PSA = TH * LDS_ROW;                      // elements per A plane
     constexpr int B_ROUNDS = CHUNK_BYTES / (GT * 16);      // 4 KB rounds per B chunk
     constexpr int B_HALF = B_ROUNDS / 2;                   // rounds each group copies
     constexpr int A_ROUNDS = GROWS * BK * 4 / (GT * 16);   // 16-byte loads per thread
-    constexpr int TM = 2;
-    static_assert(A_ROUNDS == 2 && GROWS == 2 * 32, "thread t splits rows t/8 and t/8 + 32 of its group");
+    constexpr int TM = GROWS / 32;                         // 32x32 MFMA blocks per wave
+    static_assert(A_ROUNDS == TM && GROWS == TM * 32, "thread t splits rows t/8 + 32r of its group");
     static_assert(B_ROUNDS * GT * 16 == CHUNK_BYTES && B_HALF * 2 == B_ROUNDS, "B chunk in whole half rounds");
-    __shared__ __attribute__((aligned(16))) uint16_t smA[2][chunk_elems(NP)];
+    __shared__ __attribute__((aligned(16))) uint16_t smA[2][NP * PSA];
     __shared__ __attribute__((aligned(16))) uint16_t smB[3][chunk_elems(NP)];
-    __shared__ __attribute__((aligned(16))) float stage[2][TILE * BK];
+    __shared__ __attribute__((aligned(16))) float stage[2][TH * BK];
 
     const int G = gridDim.x;
     const int slot = xcd_position(blockIdx.x, G);
@@ -472,11 +476,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     const int gtile = G % p.ntiles;   // tiles added per advance (segments: G / ntiles)
     wc.nk = p.nk;
     wc.nk_item = p.nk_item;
+    wc.th = TH;
     wc.tiles_n = p.tiles_n;
     wc.gtn = gtile % p.tiles_n;
-    wc.gm = (int64_t)(gtile / p.tiles_n) * TILE;
+    wc.gm = (int64_t)(gtile / p.tiles_n) * TH;
     wc.gseg = G / p.ntiles;
-    wc.mrows = (int64_t)(p.ntiles / p.tiles_n) * TILE;
+    wc.mrows = (int64_t)(p.ntiles / p.tiles_n) * TH;
     wc.tail_k = (int)(p.K - (int64_t)(p.nk - 1) * BK);
     wc.M = p.M;
     wc.lda = p.lda;
@@ -490,8 +495,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     const int frag_row = lane & 31;
     const int frag_k = (lane >> 5) * 8;
 
-    // Thread gt of group g loads and splits rows 64g + gt/8 + 32r (r = 0, 1),
-    // k = 4(gt%8) .. +3 of each step's FP32 A tile.
+    // Thread gt of group g loads and splits rows GROWS g + gt/8 + 32r (r <
+    // A_ROUNDS), k = 4(gt%8) .. +3 of each step's FP32 A tile.
     const int srow0 = GROWS * grp + (gt >> 3);
     const int skc = (gt & 7) * 4;
     uint32_t a_off[A_ROUNDS];
@@ -500,13 +505,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         a_off[r] = (uint32_t)(((int64_t)(srow0 + 32 * r) * p.lda + skc) * 4);
 
     // Round r (of A_ROUNDS) of the group's FP32 A rows of step w into
-    // staging buffer sb: staging is [128][32] floats, this wave's 64 lanes
-    // fill 1 KB at row 64g + 8 gw + 32 r.
+    // staging buffer sb: staging is [TH][32] floats, this wave's 64 lanes
+    // fill 1 KB at row GROWS g + 8 gw + 32 r.
     auto copy_a32_round = [&](const Walk& w, int sb, int r) __attribute__((always_inline)) {
         const float* base = p.A + w.arow + (int64_t)w.kt * BK;
-        const uint32_t dst = lds_offset(stage[sb]) + 8192 * grp + 1024 * gw;
+        const uint32_t dst = lds_offset(stage[sb]) + GROWS * BK * 4 * grp + 1024 * gw;
         uint32_t off = a_off[r];
-        if (w.rows != TILE || w.kvalid != BK) {
+        if (w.rows != TH || w.kvalid != BK) {
             // rows past M re-read the tile's last row, k past K column 0
             // (both masked when split)
             const int row = srow0 + 32 * r;
@@ -540,7 +545,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
 #pragma unroll
         for (int q = 0; q < A_ROUNDS; ++q)
             v[q] = *reinterpret_cast<const f32x4_t*>(&stage[sb][(srow0 + 32 * q) * BK + skc]);
-        if (w.rows != TILE || w.kvalid != BK) {
+        if (w.rows != TH || w.kvalid != BK) {
 #pragma unroll
             for (int q = 0; q < A_ROUNDS; ++q) {
                 const bool rok = srow0 + 32 * q < w.rows;
@@ -558,7 +563,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
             split_pieces<NP>(v[q][2], v[q][3], w1);
             uint16_t* dst = smA[ab] + split_off + 32 * q * LDS_ROW;
 #pragma unroll
-            for (int pl = 0; pl < NP; ++pl) *reinterpret_cast<u32x2_t*>(dst + pl * PS) = u32x2_t{w0[pl], w1[pl]};
+            for (int pl = 0; pl < NP; ++pl) *reinterpret_cast<u32x2_t*>(dst + pl * PSA) = u32x2_t{w0[pl], w1[pl]};
         }
     };
 
@@ -586,7 +591,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     auto load_afr = [&](int ab, int ks, int u, bf16x8_t (&af)[TM]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-            af[i] = *reinterpret_cast<const bf16x8_t*>(smA[ab] + u * PS + (grp * GROWS + i * 32) * LDS_ROW +
+            af[i] = *reinterpret_cast<const bf16x8_t*>(smA[ab] + u * PSA + (grp * GROWS + i * 32) * LDS_ROW +
                                                        (ks ? frag_off1 : frag_off0));
     };
     // The MFMAs of one plane u of A against all planes of B (fragments
@@ -703,7 +708,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         const int tile0 = SPLIT ? slot % p.ntiles : slot;
         wm.seg = SPLIT ? slot / p.ntiles : 0;
         wm.tn = tile0 % p.tiles_n;
-        wm.m0 = (int64_t)(tile0 / p.tiles_n) * TILE;
+        wm.m0 = (int64_t)(tile0 / p.tiles_n) * TH;
     }
     wm.left = my_items - 1;
     walk_start_segment(wm, wc);
@@ -890,17 +895,28 @@ int grid_for(int64_t work)
 
 using ShapeMain = Shape8;
 
+template <int NB, int TH>
+void launch_pp(const Params& p, int grid, const uint16_t* Wb, hipStream_t s)
+{
+    if (p.ksplit > 1)
+        hipLaunchKernelGGL((gemm_bf16_pp_kernel<NB, true, false, TH>), dim3(grid), dim3(512), 0, s, p, Wb);
+    else if (p.beta != 0.0f || p.bias != nullptr)
+        hipLaunchKernelGGL((gemm_bf16_pp_kernel<NB, false, true, TH>), dim3(grid), dim3(512), 0, s, p, Wb);
+    else
+        hipLaunchKernelGGL((gemm_bf16_pp_kernel<NB, false, false, TH>), dim3(grid), dim3(512), 0, s, p, Wb);
+}
+
+// fused: the two-group kernel with tiles of tile_m (128 or 64) rows; else
+// the one-barrier kernel on pre-split A (128-row tiles).
 template <int NB>
-hipError_t launch_main(const Params& p, bool fused, int grid, const uint16_t* Wb,
+hipError_t launch_main(const Params& p, bool fused, int tile_m, int grid, const uint16_t* Wb,
                        const uint16_t* Wa, hipStream_t s)
 {
     constexpr int NT = ShapeMain::NT;
-    if (fused && p.ksplit > 1)
-        hipLaunchKernelGGL((gemm_bf16_pp_kernel<NB, true, false>), dim3(grid), dim3(512), 0, s, p, Wb);
-    else if (fused && (p.beta != 0.0f || p.bias != nullptr))
-        hipLaunchKernelGGL((gemm_bf16_pp_kernel<NB, false, true>), dim3(grid), dim3(512), 0, s, p, Wb);
+    if (fused && tile_m == 64)
+        launch_pp<NB, 64>(p, grid, Wb, s);
     else if (fused)
-        hipLaunchKernelGGL((gemm_bf16_pp_kernel<NB, false, false>), dim3(grid), dim3(512), 0, s, p, Wb);
+        launch_pp<NB, 128>(p, grid, Wb, s);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<ShapeMain, NB, false>), dim3(grid), dim3(NT), 0, s, p, Wb, Wa);
     return hipGetLastError();
@@ -985,18 +1001,20 @@ hipError_t launch_presplit_b(const float* B, int64_t ldb, bool trans_b, int64_t 
                            planes, stream);
 }
 
-hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const DeviceInfo& dev,
-                            void* workspace, hipStream_t stream)
+hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, int tile_m,
+                            const DeviceInfo& dev, void* workspace, hipStream_t stream)
 {
     if (nbands != 5 && nbands != 3 && nbands != 2 && nbands != 1) return hipErrorInvalidValue;
-    const int64_t tiles_m = (g.M + TILE - 1) / TILE;
+    if (tile_m != 128 && tile_m != 64) return hipErrorInvalidValue;
+    const bool fused = fused_a_path(g);
+    if (!fused) tile_m = TILE;   // the pre-split kernel has 128-row tiles only
+    const int64_t tiles_m = (g.M + tile_m - 1) / tile_m;
     const int64_t tiles_n = (g.N + TILE - 1) / TILE;
     const int64_t nk = (g.K + BK - 1) / BK;
     const int64_t lim = (int64_t)1 << 31;
     if (tiles_m * tiles_n >= lim || tiles_m * tiles_n * nk >= lim || tiles_n * nk >= lim ||
         tiles_m * nk >= lim)
         return hipErrorInvalidValue;
-    const bool fused = fused_a_path(g);
     const WsLayout lay = ws_layout(g, nbands, ksplit);
     if (ksplit < 1 || nk % ksplit != 0 || (ksplit > 1 && !fused) ||
         tiles_m * tiles_n * ksplit >= lim || (workspace == nullptr && lay.total > 0) ||
@@ -1046,10 +1064,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, const Dev
         const int64_t items = (int64_t)p.ntiles * ksplit;
         const int grid = items < dev.num_cu ? (int)items : dev.num_cu;
         switch (nbands) {
-        case 5: e = launch_main<5>(p, fused, grid, Wb, Wa, stream); break;
-        case 3: e = launch_main<3>(p, fused, grid, Wb, Wa, stream); break;
-        case 2: e = launch_main<2>(p, fused, grid, Wb, Wa, stream); break;
-        default: e = launch_main<1>(p, fused, grid, Wb, Wa, stream); break;
+        case 5: e = launch_main<5>(p, fused, tile_m, grid, Wb, Wa, stream); break;
+        case 3: e = launch_main<3>(p, fused, tile_m, grid, Wb, Wa, stream); break;
+        case 2: e = launch_main<2>(p, fused, tile_m, grid, Wb, Wa, stream); break;
+        default: e = launch_main<1>(p, fused, tile_m, grid, Wb, Wa, stream); break;
         }
     }
     if (e == hipSuccess && ksplit > 1) {

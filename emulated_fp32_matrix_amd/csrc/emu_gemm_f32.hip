@@ -303,6 +303,7 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_pp_kernel(Params p, const flo
     const int gtile = G % p.ntiles;
     wc.nk = p.nk;
     wc.nk_item = p.nk;
+    wc.th = TILE;
     wc.tiles_n = p.tiles_n;
     wc.gtn = gtile % p.tiles_n;
     wc.gm = (int64_t)(gtile / p.tiles_n) * TILE;

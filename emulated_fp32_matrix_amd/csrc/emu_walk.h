@@ -21,7 +21,7 @@ struct Walk {
     int left;        // items after this one
     int64_t m0;      // first row
     int64_t arow;    // m0 * lda (element offset of the tile's first A row)
-    int rows;        // rows of the tile inside op(A): min(M - m0, TILE)
+    int rows;        // rows of the tile inside op(A): min(M - m0, th)
     int kvalid;      // k of this step inside op(A): min(K - 32 kt, 32)
 };
 
@@ -33,14 +33,15 @@ struct TilePos {
 
 struct WalkConst {
     int nk, nk_item, tiles_n, gtn, gseg, tail_k;   // tail_k: valid k of the last step
-    int64_t gm, mrows, M, lda;   // gm: rows added per advance; mrows: tiles_m * TILE
+    int th;                      // rows of an output tile
+    int64_t gm, mrows, M, lda;   // gm: rows added per advance; mrows: tiles_m * th
 };
 
 __device__ __forceinline__ void walk_set_tile(Walk& w, const WalkConst& c)
 {
     w.arow = w.m0 * c.lda;
     const int64_t r = c.M - w.m0;
-    w.rows = r < TILE ? (int)r : TILE;
+    w.rows = r < c.th ? (int)r : c.th;
 }
 
 __device__ __forceinline__ void walk_start_segment(Walk& w, const WalkConst& c)
@@ -62,7 +63,7 @@ __device__ __forceinline__ void walk_next(Walk& w, const WalkConst& c)
         w.m0 += c.gm;
         if (w.tn >= c.tiles_n) {
             w.tn -= c.tiles_n;
-            w.m0 += TILE;
+            w.m0 += c.th;
         }
         if constexpr (SPLIT) {
             w.seg += c.gseg;

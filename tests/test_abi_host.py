@@ -178,7 +178,7 @@ def test_ksplit_choice_is_pure_and_follows_the_cost_model():
     for M, N, K in [(552960, 768, 256), (552960, 256, 768), (4096, 4096, 4096), (0, 5, 5),
                     (5, 5, 0)]:
         assert emu.select_ksplit(M, N, K) == 1, (M, N, K)
-    for M, N, K in [(6144, 256, 768), (2048, 256, 4096), (1024, 512, 8192)]:
+    for M, N, K in [(512, 256, 4096), (2048, 256, 4096), (1024, 512, 8192)]:
         S = emu.select_ksplit(M, N, K)
         nk = -(-K // 32)
         assert 1 < S <= 8 and nk % S == 0, (M, N, K, S)
