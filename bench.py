@@ -69,8 +69,31 @@ KERNEL_SOURCES = ("emulated_fp32_matrix_amd/csrc/emu_gemm_bf16.hip",
 # WRITE_SIZE) scaled by the same counters' reading for a 1 GiB device copy.
 # Keyed by the SHA-256 of KERNEL_SOURCES: a changed kernel reports null.
 TRAFFIC_BY_SOURCE = {
-    "6d1e43fa7e78712fe334ec350389c3cfcc35d2785a54f81f9a0e7f78b2f97698": 1892241080,
+    "251f8416ac528fdc389cb2505fc59e2762bafdb9c3ee7accad4565a12b8ea34c": 1973219017,
 }
+
+
+# Shader clock of the main BF16X9 kernel over this workload (GHz), from a
+# rocprofv3 pass with GRBM_GUI_ACTIVE (GPU-busy cycles at the shader clock,
+# summed over the 8 XCDs) and the kernel trace of the same dispatches:
+# sum(GRBM_GUI_ACTIVE / 8) / sum(duration) over the launches of the timed steps.
+# Keyed like TRAFFIC_BY_SOURCE; a changed kernel reports null.
+SCLK_BY_SOURCE = {
+    "251f8416ac528fdc389cb2505fc59e2762bafdb9c3ee7accad4565a12b8ea34c": 1.748,
+}
+SPEC_SCLK_GHZ = 2.4         # the clock of the spec peaks
+
+
+def cpu_model():
+    """The host CPU's model name (first 'model name' of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def kernel_source_hash():
@@ -178,7 +201,7 @@ def cpu_baseline(gemms, target_s):
         flops += 2 * rows * g.N * g.K
     el = time.time() - t0
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
             "sample": (f"first {rows} of 552,960 rows of each of the 8 GEMMs "
                        f"({flops / 1e9:.1f} GFLOP, {el:.1f} s, BF16X9 model: exact split + "
                        "FP32 band accumulation, OpenMP over rows)")}
@@ -223,12 +246,18 @@ def main():
     avg_us = float(per.sum()) / n_launch * 1e3
     peak = BF16_PEAK_TFLOPS if mode in BANDS else F32_PEAK_TFLOPS
     achieved = P * float(flops.sum()) / n_launch / (avg_us * 1e-6) / 1e12
-    traffic = None
+    traffic = sclk = None
     if mode == "BF16X9":
-        traffic = TRAFFIC_BY_SOURCE.get(kernel_source_hash())
+        src = kernel_source_hash()
+        traffic = TRAFFIC_BY_SOURCE.get(src)
+        sclk = SCLK_BY_SOURCE.get(src)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel": ("gemm_bf16_pp_kernel<%d, false>" % BANDS[mode])
+                # the same fraction against the peak at the clock the kernel ran at
+                "sclk_ghz": sclk,
+                "frac_at_measured_clock": (round(achieved / (peak * sclk / SPEC_SCLK_GHZ), 4)
+                                           if sclk else None),
+                "kernel": ("gemm_bf16_pp_kernel<%d, false, false, 128>" % BANDS[mode])
                 if mode in BANDS else "gemm_f32_pp_kernel",
                 "avg_launch_us": round(avg_us, 2),
                 "algorithmic_flop_per_launch": round(P * float(flops.sum()) / n_launch)}
