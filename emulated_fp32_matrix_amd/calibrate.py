@@ -87,17 +87,31 @@ def measure(modes=("NATIVE_F32", "BF16X9")):
 
 # ---- the cost model (same form as predict_x9_us / predict_us in csrc/emu_api.hip) ----
 PARAMS = ("x9_fixed", "x9_step_part", "x9_step_full", "f32_fixed", "f32_step_part", "f32_step_full")
+# A k-step of the emulated kernel's 64-row tiles against a 128-row one
+# (kX9Step64): measured separately, with the tile height forced, on the
+# 552,960-row stack where every CU is busy either way; not fitted here.
+X9_STEP64 = 0.59
+
+
+def predict_x9(M, N, K, p, tile_m):
+    tiles = math.ceil(M / tile_m) * math.ceil(N / 128)
+    nk = math.ceil(K / 32)
+    step = (p["x9_step_full"] if tiles >= 256 else p["x9_step_part"]) * (X9_STEP64 if tile_m == 64 else 1.0)
+    return p["x9_fixed"] + math.ceil(tiles / 256) * nk * step
 
 
 def predict(M, N, K, p):
     """(native, BF16X9 unsplit) predicted device time in microseconds: both
-    kernels keep one 128x128 tile per CU and run ceil(tiles / 256) rounds of
-    nk k-steps, each step costing *_step_full once every CU has a tile and
-    *_step_part before."""
+    kernels run ceil(tiles / 256) rounds of nk k-steps, each step costing
+    *_step_full once every CU has a tile and *_step_part before; the
+    emulated kernel's tiles have 128 rows, or 64 where that is predicted at
+    least 3 % faster (the library's choose_tile_m), a 64-row step costing
+    X9_STEP64 of a 128-row one."""
     tiles = math.ceil(M / 128) * math.ceil(N / 128)
     nk = math.ceil(K / 32)
     full = tiles >= 256
-    x9 = p["x9_fixed"] + math.ceil(tiles / 256) * nk * (p["x9_step_full"] if full else p["x9_step_part"])
+    x9_128, x9_64 = predict_x9(M, N, K, p, 128), predict_x9(M, N, K, p, 64)
+    x9 = x9_64 if x9_64 < 0.97 * x9_128 else x9_128
     f32 = p["f32_fixed"] + math.ceil(tiles / 256) * nk * (p["f32_step_full"] if full else p["f32_step_part"])
     return f32, x9
 
