@@ -69,7 +69,7 @@ KERNEL_SOURCES = ("emulated_fp32_matrix_amd/csrc/emu_gemm_bf16.hip",
 # WRITE_SIZE) scaled by the same counters' reading for a 1 GiB device copy.
 # Keyed by the SHA-256 of KERNEL_SOURCES: a changed kernel reports null.
 TRAFFIC_BY_SOURCE = {
-    "251f8416ac528fdc389cb2505fc59e2762bafdb9c3ee7accad4565a12b8ea34c": 1973219017,
+    "bdcdf111e991602f3f57b8fcd0c2018b43080069b1718fe08138c2bc7f79b813": 1985636907,
 }
 
 
@@ -79,7 +79,7 @@ TRAFFIC_BY_SOURCE = {
 # sum(GRBM_GUI_ACTIVE / 8) / sum(duration) over the launches of the timed steps.
 # Keyed like TRAFFIC_BY_SOURCE; a changed kernel reports null.
 SCLK_BY_SOURCE = {
-    "251f8416ac528fdc389cb2505fc59e2762bafdb9c3ee7accad4565a12b8ea34c": 1.748,
+    "bdcdf111e991602f3f57b8fcd0c2018b43080069b1718fe08138c2bc7f79b813": 1.735,
 }
 SPEC_SCLK_GHZ = 2.4         # the clock of the spec peaks
 

@@ -9,7 +9,7 @@ this package fails if the library has not been built, and every call raises
 Low-level entry points mirror the C ABI one to one (pointers are ints):
 :func:`emu_sgemm`, :func:`emu_sgemm_bias`, :func:`emu_sgemm_ex`,
 :func:`emu_sgemm_noalloc`, :func:`emu_split_bf16x3`, :func:`emu_sgemm_select`, :func:`emu_sgemm_ksplit`,
-:func:`emu_status_string`, :func:`emu_abi_version`.  :func:`sgemm` and
+:func:`emu_sgemm_plan`, :func:`emu_status_string`, :func:`emu_abi_version`.  :func:`sgemm` and
 :func:`split_bf16x3` accept torch tensors.
 
 Method: "Unlocking Tensor Core Performance for Machine Learning Interatomic
@@ -35,11 +35,12 @@ STATUS_ALLOC_FAILED = 4
 STATUS_INTERNAL = 5
 STATUS_SCRATCH_TOO_SMALL = 6
 NOALLOC_SCRATCH_BYTES = 64 << 20   # EMU_NOALLOC_SCRATCH_BYTES
+KSPLIT_AUTO = -1                   # EMU_KSPLIT_AUTO: the AUTO policy's plan in an explicit mode
 
 # C functions declared in include/emu_sgemm.h
 EXPORTS = ("emu_sgemm", "emu_sgemm_bias", "emu_sgemm_ex", "emu_split_bf16x3", "emu_sgemm_select",
            "emu_sgemm_ksplit", "emu_presplit_b_bytes", "emu_presplit_b", "emu_sgemm_presplit",
-           "emu_sgemm_noalloc", "emu_status_string", "emu_abi_version")
+           "emu_sgemm_noalloc", "emu_sgemm_plan", "emu_status_string", "emu_abi_version")
 
 
 class EmuError(RuntimeError):
@@ -78,6 +79,9 @@ _lib.emu_sgemm_noalloc.argtypes = _lib.emu_sgemm_ex.argtypes
 _lib.emu_sgemm_noalloc.restype = ctypes.c_int
 _lib.emu_sgemm_ksplit.argtypes = [_i64, _i64, _i64, ctypes.POINTER(ctypes.c_int)]
 _lib.emu_sgemm_ksplit.restype = ctypes.c_int
+_lib.emu_sgemm_plan.argtypes = [_i64, _i64, _i64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                ctypes.POINTER(ctypes.c_int64)]
+_lib.emu_sgemm_plan.restype = ctypes.c_int
 _lib.emu_presplit_b_bytes.argtypes = [_i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
 _lib.emu_presplit_b_bytes.restype = ctypes.c_int
 _lib.emu_presplit_b.argtypes = [ctypes.c_int, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, _vp]
@@ -151,6 +155,14 @@ def emu_sgemm_ksplit(M, N, K):
     return st, (out.value if st == STATUS_SUCCESS else None)
 
 
+def emu_sgemm_plan(M, N, K):
+    """(status, (ksplit, tile_rows, split_from) of the AUTO plan, or None)."""
+    sp, th, sf = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_int64(-1)
+    st = int(_lib.emu_sgemm_plan(int(M), int(N), int(K), ctypes.byref(sp), ctypes.byref(th),
+                                 ctypes.byref(sf)))
+    return st, ((sp.value, th.value, sf.value) if st == STATUS_SUCCESS else None)
+
+
 def emu_presplit_b_bytes(N, K, mode):
     """(status, bytes) of emu_presplit_b_bytes."""
     out = ctypes.c_size_t(0)
@@ -217,7 +229,8 @@ def sgemm(a, b, mode="BF16X9", trans_a=False, trans_b=False, alpha=1.0, beta=0.0
     """C = alpha * op(a) @ op(b) + beta * c (+ bias[j] on every row) through
     ``emu_sgemm`` (``emu_sgemm_bias`` when ``bias`` is given, ``emu_sgemm_ex``
     when ``ksplit`` is given: 0 = the library's choice, S >= 1 = exactly S
-    K segments).
+    K segments on every output tile, ``KSPLIT_AUTO`` = the AUTO policy's plan
+    in the mode given).
 
     ``a``/``b`` are the stored (row-major) matrices; ``trans_*`` select op().
     Returns ``c`` (allocated when None).  Asynchronous on ``stream``
@@ -358,3 +371,13 @@ def select_ksplit(M, N, K) -> int:
     if st != STATUS_SUCCESS:
         raise EmuError(st, "emu_sgemm_ksplit")
     return sp
+
+
+def select_plan(M, N, K):
+    """(ksplit, tile_rows, split_from) of the AUTO policy's emulated plan:
+    tiles of tile_rows x 128, numbered row by row, those from split_from on
+    split into ksplit K segments."""
+    st, plan = emu_sgemm_plan(M, N, K)
+    if st != STATUS_SUCCESS:
+        raise EmuError(st, "emu_sgemm_plan")
+    return plan

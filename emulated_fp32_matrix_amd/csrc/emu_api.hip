@@ -215,58 +215,101 @@ constexpr double kX9Step64 = 0.59;
 
 double ceil_div(double a, double b) { return std::ceil(a / b); }
 
+// A launch of the emulated kernel: K segments, rows of an output tile, and
+// the first tile whose K is split (0: all of them, when split > 1).  With
+// split_from > 0 the tiles before it (whole rounds of 256) run unsplit and
+// only the last, partly filled round's tiles are split: the items of that
+// round then fill the CUs.
+struct Plan {
+    int split = 1;
+    int tile_m = 128;
+    int64_t split_from = 0;
+};
+
+double predict_plan_us(int64_t M, int64_t N, int64_t K, const Plan& pl)
+{
+    const double tiles = ceil_div((double)M, (double)pl.tile_m) * ceil_div((double)N, 128.0);
+    const double nk = ceil_div((double)K, 32.0);
+    const double f64 = pl.tile_m == 64 ? kX9Step64 : 1.0;
+    if (pl.split == 1) {
+        const double step = (tiles >= kCUs ? kX9StepFull : kX9StepPart) * f64;
+        return kX9Fixed + ceil_div(tiles, kCUs) * nk * step;
+    }
+    const double whole = (double)pl.split_from;   // tiles of the unsplit rounds
+    const double items = (tiles - whole) * pl.split;
+    double t = kX9Fixed + whole / kCUs * nk * kX9StepFull * f64;
+    t += ceil_div(items, kCUs) * (nk / pl.split) * (items + whole >= kCUs ? kX9StepFull : kX9StepPart) * f64;
+    const double elems = pl.split_from == 0 ? (double)M * (double)N : (tiles - whole) * pl.tile_m * 128.0;
+    return t + kRedFixed + (double)(pl.split + 1) * elems * 4.0 / kRedBytesPerUs;
+}
+
 double predict_x9_us(int64_t M, int64_t N, int64_t K, int split, int tile_m)
 {
-    const double tiles = ceil_div((double)M, (double)tile_m) * ceil_div((double)N, 128.0);
-    const double nk = ceil_div((double)K, 32.0);
-    const double items = tiles * split;
-    const double step = (items >= kCUs ? kX9StepFull : kX9StepPart) * (tile_m == 64 ? kX9Step64 : 1.0);
-    double t = kX9Fixed + ceil_div(items, kCUs) * (nk / split) * step;
-    if (split > 1) t += kRedFixed + (double)(split + 1) * (double)M * (double)N * 4.0 / kRedBytesPerUs;
-    return t;
+    Plan pl;
+    pl.split = split;
+    pl.tile_m = tile_m;
+    return predict_plan_us(M, N, K, pl);
 }
 
 // The rows of the emulated kernel's output tiles for a call with `split` K
-// segments (fused-A path; the result does not depend on it): 64 where the
-// cost model predicts them at least 3 % faster than 128-row tiles (too few
-// 128-row tiles to fill the CUs, or a last round of tiles mostly idle).
+// segments over every tile (fused-A path; the result does not depend on
+// it): 64 where the cost model predicts them at least 3 % faster than
+// 128-row tiles (too few 128-row tiles to fill the CUs, or a last round of
+// tiles mostly idle).
 int choose_tile_m(int64_t M, int64_t N, int64_t K, int split)
 {
     if (M == 0 || N == 0 || K == 0) return 128;
     return predict_x9_us(M, N, K, split, 64) < 0.97 * predict_x9_us(M, N, K, split, 128) ? 64 : 128;
 }
 
-double predict_x9_best_us(int64_t M, int64_t N, int64_t K, int split)
+// The plan the emulated path uses by itself (fused-A path), from the cost
+// model: for each divisor S <= kMaxSplit of ceil(K/32), every tile split
+// (its tile height by the 3 % rule above) and, where the tiles leave a last
+// round partly filled, only that round split (for each tile height); the
+// fastest of these, and no split (tile height by the same rule) unless that
+// saves at least 5 %.
+Plan choose_plan(int64_t M, int64_t N, int64_t K)
 {
-    return predict_x9_us(M, N, K, split, choose_tile_m(M, N, K, split));
-}
-
-// The K split the emulated path uses by itself (fused-A path): the divisor
-// S <= kMaxSplit of ceil(K/32) with the least predicted time (each with its
-// own tile choice), and 1 unless that saves at least 5 %.
-int choose_ksplit(int64_t M, int64_t N, int64_t K)
-{
-    if (M == 0 || N == 0 || K == 0) return 1;
+    Plan base;
+    if (M == 0 || N == 0 || K == 0) return base;
+    base.tile_m = choose_tile_m(M, N, K, 1);
+    const double t1 = predict_plan_us(M, N, K, base);
     const int64_t nk = (K + 31) / 32;
-    const double t1 = predict_x9_best_us(M, N, K, 1);
-    int best = 1;
+    const int64_t tiles_n = (N + 127) / 128;
+    Plan best = base;
     double tbest = t1;
-    for (int sp = 2; sp <= kMaxSplit && sp <= nk; ++sp) {
-        if (nk % sp != 0) continue;
-        const double t = predict_x9_best_us(M, N, K, sp);
+    auto consider = [&](const Plan& pl) {
+        const double t = predict_plan_us(M, N, K, pl);
         if (t < tbest) {
             tbest = t;
-            best = sp;
+            best = pl;
+        }
+    };
+    for (int sp = 2; sp <= kMaxSplit && sp <= nk; ++sp) {
+        if (nk % sp != 0) continue;
+        Plan all;
+        all.split = sp;
+        all.tile_m = choose_tile_m(M, N, K, sp);
+        consider(all);
+        for (int th : {128, 64}) {
+            const int64_t tiles = (M + th - 1) / th * tiles_n;
+            const int64_t full = tiles / (int64_t)kCUs * (int64_t)kCUs;
+            if (full == 0 || full == tiles) continue;
+            Plan tail;
+            tail.split = sp;
+            tail.tile_m = th;
+            tail.split_from = full;
+            consider(tail);
         }
     }
-    return tbest < 0.95 * t1 ? best : 1;
+    return tbest < 0.95 * t1 ? best : base;
 }
 
 void predict_us(int64_t M, int64_t N, int64_t K, double& f32, double& x9)
 {
     const double tiles = ceil_div((double)M, 128.0) * ceil_div((double)N, 128.0);
     const double nk = ceil_div((double)K, 32.0);
-    x9 = predict_x9_best_us(M, N, K, choose_ksplit(M, N, K));
+    x9 = predict_plan_us(M, N, K, choose_plan(M, N, K));
     f32 = kF32Fixed + ceil_div(tiles, kCUs) * nk * (tiles >= kCUs ? kF32StepFull : kF32StepPart);
 }
 
@@ -307,7 +350,7 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     if (!valid_op(transA) || !valid_op(transB)) return EMU_STATUS_INVALID_VALUE;
     if ((int)mode < (int)EMU_MODE_NATIVE_F32 || (int)mode > (int)EMU_MODE_BF16X1)
         return EMU_STATUS_INVALID_VALUE;
-    if (ksplit < 0 || (ksplit > 0 && !emulated(mode))) return EMU_STATUS_INVALID_VALUE;
+    if (ksplit < EMU_KSPLIT_AUTO || (ksplit != 0 && !emulated(mode))) return EMU_STATUS_INVALID_VALUE;
     if (ksplit > 1 && (K == 0 || ((K + 31) / 32) % ksplit != 0)) return EMU_STATUS_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return EMU_STATUS_INVALID_VALUE;
     if (lda < (transA == EMU_OP_N ? max1(K) : max1(M))) return EMU_STATUS_INVALID_VALUE;
@@ -369,8 +412,26 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     if (ksplit > 1 && !fused) return EMU_STATUS_NOT_SUPPORTED;
     // ksplit 0: the performant policy (AUTO) may split where its cost model
     // predicts a gain; an explicit mode computes without a split, so a row
-    // of C never depends on the other rows.
-    if (ksplit == 0) ksplit = auto_mode && fused ? choose_ksplit(M, N, K) : 1;
+    // of C never depends on the other rows.  EMU_KSPLIT_AUTO: the policy's
+    // plan in an explicit mode.  S > 1: every tile split.
+    Plan plan;
+    if (ksplit == EMU_KSPLIT_AUTO || (ksplit == 0 && auto_mode)) {
+        if (fused) {
+            plan = choose_plan(M, N, K);
+            // a split of the last round only needs whole rounds of this
+            // device's compute units before it
+            const int64_t tiles = (M + plan.tile_m - 1) / plan.tile_m * ((N + 127) / 128);
+            const int64_t round = tiles < dev.num_cu ? tiles : dev.num_cu;
+            if (plan.split_from % round != 0) plan.split_from = 0;
+        } else {
+            plan.tile_m = choose_tile_m(M, N, K, 1);
+        }
+    } else if (ksplit > 1) {
+        plan.split = ksplit;
+        plan.tile_m = choose_tile_m(M, N, K, ksplit);
+    } else {
+        plan.tile_m = choose_tile_m(M, N, K, 1);
+    }
     int nbands;
     switch (mode) {
     case EMU_MODE_BF16X9: nbands = 5; break;
@@ -380,12 +441,12 @@ emu_status_t sgemm_impl(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, 
     default: return EMU_STATUS_INTERNAL;
     }
     void* ws = nullptr;
-    const size_t ws_bytes = emu::gemm_bf16_workspace_bytes(g, nbands, ksplit);
+    const size_t ws_bytes = emu::gemm_bf16_workspace_bytes(g, nbands, plan.split, plan.tile_m, plan.split_from);
     if (ws_bytes > 0) {
         const emu_status_t st = workspace(ws_bytes, &ws);
         if (st != EMU_STATUS_SUCCESS) return st;
     }
-    return from_hip(emu::launch_gemm_bf16(g, nbands, ksplit, choose_tile_m(M, N, K, ksplit), dev, ws, s));
+    return from_hip(emu::launch_gemm_bf16(g, nbands, plan.split, plan.split_from, plan.tile_m, dev, ws, s));
 }
 
 // Bands of an emulated mode (0 for NATIVE_F32 and AUTO).
@@ -418,7 +479,7 @@ const char* emu_status_string(emu_status_t status)
     }
 }
 
-int emu_abi_version(void) { return 106; }
+int emu_abi_version(void) { return 107; }
 
 emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N, int64_t K,
                               emu_mode_t* chosen)
@@ -498,7 +559,19 @@ emu_status_t emu_sgemm_noalloc(emu_op_t transA, emu_op_t transB, int64_t M, int6
 emu_status_t emu_sgemm_ksplit(int64_t M, int64_t N, int64_t K, int* ksplit)
 {
     if (M < 0 || N < 0 || K < 0 || ksplit == nullptr) return EMU_STATUS_INVALID_VALUE;
-    *ksplit = choose_ksplit(M, N, K);
+    *ksplit = choose_plan(M, N, K).split;
+    return EMU_STATUS_SUCCESS;
+}
+
+emu_status_t emu_sgemm_plan(int64_t M, int64_t N, int64_t K, int* ksplit, int* tile_rows,
+                            int64_t* split_from)
+{
+    if (M < 0 || N < 0 || K < 0 || ksplit == nullptr || tile_rows == nullptr || split_from == nullptr)
+        return EMU_STATUS_INVALID_VALUE;
+    const Plan pl = choose_plan(M, N, K);
+    *ksplit = pl.split;
+    *tile_rows = pl.tile_m;
+    *split_from = pl.split == 1 ? ((M + pl.tile_m - 1) / pl.tile_m) * ((N + 127) / 128) : pl.split_from;
     return EMU_STATUS_SUCCESS;
 }
 

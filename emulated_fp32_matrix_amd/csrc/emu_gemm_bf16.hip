@@ -449,7 +449,7 @@ __global__ __launch_bounds__(SH::NT, 1) void gemm_bf16_kernel(Params p, const ui
 template <int NB, bool SPLIT, bool GENERAL, int TH>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const uint16_t* __restrict__ Wb)
 {
-    static_assert(!(SPLIT && GENERAL), "a split K adds beta C and the bias in the reduction");
+    static_assert(!(SPLIT && GENERAL), "a split launch reads beta and the bias at run time");
     static_assert(TH == 128 || TH == 64, "output tiles of 128 or 64 rows");
     constexpr int NP = NB >= 3 ? 3 : NB;
     constexpr int CHUNK_BYTES = (int)chunk_elems(NP) * 2;
@@ -468,20 +468,27 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
 
     const int G = gridDim.x;
     const int slot = xcd_position(blockIdx.x, G);
-    const int nitems = SPLIT ? p.ntiles * p.ksplit : p.ntiles;
+    // Items: tiles 0 .. split_from-1 whole, then (SPLIT) the ksplit K
+    // segments of each of the other tiles; this workgroup's are slot, slot +
+    // G, ...  (split_from is 0, every tile split, or a multiple of G: whole
+    // rounds of whole tiles, then the last round's tiles split.)
+    const int nsplit = SPLIT ? p.ntiles - p.split_from : 0;
+    const int nitems = SPLIT ? p.split_from + nsplit * p.ksplit : p.ntiles;
     const int my_items = (nitems - slot + G - 1) / G;
-    const int total = my_items * (SPLIT ? p.nk_item : p.nk);
+    const int my_whole = SPLIT ? (slot < p.split_from ? (p.split_from - slot + G - 1) / G : 0) : my_items;
+    const int total = my_whole * p.nk + (my_items - my_whole) * p.nk_item;
 
     WalkConst wc;
-    const int gtile = G % p.ntiles;   // tiles added per advance (segments: G / ntiles)
+    const int gtile = G % p.ntiles;   // tiles added per advance
     wc.nk = p.nk;
     wc.nk_item = p.nk_item;
     wc.th = TH;
+    wc.G = G;
+    wc.split_from = SPLIT ? p.split_from : p.ntiles;
+    wc.nsplit = nsplit > 0 ? nsplit : 1;
     wc.tiles_n = p.tiles_n;
     wc.gtn = gtile % p.tiles_n;
     wc.gm = (int64_t)(gtile / p.tiles_n) * TH;
-    wc.gseg = G / p.ntiles;
-    wc.mrows = (int64_t)(p.ntiles / p.tiles_n) * TH;
     wc.tail_k = (int)(p.K - (int64_t)(p.nk - 1) * BK);
     wc.M = p.M;
     wc.lda = p.lda;
@@ -610,27 +617,42 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
         }
     };
 
-    // Epilogue of this wave's 64x32 block of the item at w: bands recombined
-    // smallest first into t, then C = alpha t + beta C + bias, or with a
-    // split K (PART) t itself into the segment's slice of the workspace.
-    // Lane l holds, per 32x32 block and register group q, row l%32 and
-    // columns 8q + 4(l/32) .. +3: one 16-byte buffer store each, rows outside
-    // C given an out-of-range offset.  Tiles that cross column N, or a
-    // destination without 16-byte rows, store element by element.  SCALE:
-    // alpha != 1.
-    auto epilogue = [&]<bool SCALE, bool PART>(const TilePos& w) __attribute__((always_inline)) {
+    // Epilogue of this wave's block of the item at w: bands recombined
+    // smallest first into t, then C = alpha t + beta C + bias, or for a K
+    // segment of a split tile (part) t itself into the segment's slot of the
+    // workspace (TH x 128 floats, rows of 128).  Lane l holds, per 32x32
+    // block and register group q, row l%32 and columns 8q + 4(l/32) .. +3:
+    // one 16-byte buffer store each, rows outside C given an out-of-range
+    // offset.  Tiles that cross column N, or a destination without 16-byte
+    // rows, store element by element.  SCALE: alpha != 1.
+    // In a split launch one copy serves both kinds of item, its destination
+    // and scalars chosen at run time (a part: alpha 1, which is exact, no
+    // beta, no bias; a whole tile takes them here, a split one in the
+    // reduction).
+    auto epilogue = [&]<bool SCALE>(const TilePos& w) __attribute__((always_inline)) {
         const int64_t n0 = (int64_t)w.tn * TILE;
-        const int64_t ldd = PART ? p.N : p.ldc;
-        float* const dst = PART ? p.wsC + (int64_t)w.seg * p.M * p.N + w.m0 * p.N + n0
-                                : p.C + w.m0 * p.ldc + n0;
-        const float beta = GENERAL ? p.beta : 0.0f;
-        const float* const bias = GENERAL ? p.bias : nullptr;
+        int64_t ldd = p.ldc;
+        float* dst = p.C + w.m0 * p.ldc + n0;
+        float alpha = p.alpha;
+        float beta = GENERAL || SPLIT ? p.beta : 0.0f;
+        const float* bias = GENERAL || SPLIT ? p.bias : nullptr;
+        bool part = false;
+        if constexpr (SPLIT) {
+            part = w.part != 0;
+            if (part) {
+                ldd = TILE;
+                dst = p.wsC + (int64_t)w.widx * (TH * TILE);
+                alpha = 1.0f;
+                beta = 0.0f;
+                bias = nullptr;
+            }
+        }
         const __amdgpu_buffer_rsrc_t rsrc =
             __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, 0x7FFFFFFF, 0x00020000);
         const int64_t cl = p.N - n0;
         const int cols_left = cl < TILE ? (int)cl : TILE;
         // vec_b / vec_ws carry the destination's (and the bias') alignment
-        const bool vec_c = (PART ? p.vec_ws : p.vec_b) != 0 && cols_left == TILE;
+        const bool vec_c = (part ? p.vec_ws : p.vec_b) != 0 && cols_left == TILE;
         const int ldd4 = (int)ldd * 4;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -646,7 +668,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
                     float sum = acc[i][NB - 1][r];
 #pragma unroll
                     for (int b = NB - 2; b >= 0; --b) sum = __builtin_fmaf(sum, 0.00390625f, acc[i][b][r]);
-                    out[e] = SCALE ? p.alpha * sum : sum;
+                    out[e] = SCALE ? alpha * sum : sum;
                 }
                 if (vec_c) {
                     const int off = row_ok ? row * ldd4 + col * 4 : (int)0x80000000;
@@ -692,11 +714,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     const bool unit_alpha = p.alpha == 1.0f;
     auto epilogue_any = [&](const TilePos& w) __attribute__((always_inline)) {
         if constexpr (SPLIT)
-            epilogue.template operator()<false, true>(w);
+            epilogue.template operator()<true>(w);
         else if (unit_alpha)
-            epilogue.template operator()<false, false>(w);
+            epilogue.template operator()<false>(w);
         else
-            epilogue.template operator()<true, false>(w);
+            epilogue.template operator()<true>(w);
     };
 
     // Cursors: wm = step of the next M phase, we = the step before it (its
@@ -704,18 +726,23 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
     // step after it (split, and its B chunk loaded, in the next U phase),
     // wa = the step of the next A load.
     Walk wm;
-    {
-        const int tile0 = SPLIT ? slot % p.ntiles : slot;
-        wm.seg = SPLIT ? slot / p.ntiles : 0;
-        wm.tn = tile0 % p.tiles_n;
-        wm.m0 = (int64_t)(tile0 / p.tiles_n) * TH;
+    if constexpr (SPLIT) {
+        walk_set_item(wm, wc, slot);
+    } else {
+        wm.seg = 0;
+        wm.tn = slot % p.tiles_n;
+        wm.m0 = (int64_t)(slot / p.tiles_n) * TH;
+        wm.kt = 0;
+        wm.kt_end = p.nk;
+        wm.item = slot;
+        wm.part = 0;
+        wm.widx = 0;
+        walk_set_tile(wm, wc);
     }
     wm.left = my_items - 1;
-    walk_start_segment(wm, wc);
-    walk_set_tile(wm, wc);
     wm.kvalid = wm.kt + 1 < p.nk ? BK : wc.tail_k;
     Walk ws = wm, wa = wm;
-    TilePos we{wm.m0, wm.tn, wm.rows, wm.seg};
+    TilePos we{wm.m0, wm.tn, wm.rows, wm.seg, wm.part, wm.widx};
     // Prologue: B chunk of step 0 (each group its half) and group 1's half
     // of B chunk 1, then the FP32 A rows of steps 0 and 1, all issued before
     // one wait that leaves only the step-1 rows in flight (U(0) waits for
@@ -815,7 +842,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
             }
         }
         epi = wm.kt == (SPLIT ? wm.kt_end : p.nk) - 1;
-        we = TilePos{wm.m0, wm.tn, wm.rows, wm.seg};
+        we = TilePos{wm.m0, wm.tn, wm.rows, wm.seg, wm.part, wm.widx};
         // wm, ws, wa are the same sequence one and two steps apart (past the
         // end all stay on the last step): one advance, two copies
         wm = ws;
@@ -838,56 +865,66 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(Params p, const ui
 }
 
 // ---------------------------------------------------------------------------
-// Reduction of a split K: C = alpha (t_0 + t_1 + ... + t_{S-1}) + beta C
-// + bias, the segments' results added in segment order, each step one FP32
-// operation (C not read when beta == 0).  ws holds S slices of M x N (leading
-// dimension N).  Threads walk rows (blockIdx.y, strided) and 4-column groups
-// (VEC: 16-byte loads and stores; N % 4 == 0, C rows and bias 16-byte
+// Reduction of the split tiles: for split tile i (tile split_from + i),
+// C = alpha (t_0 + t_1 + ... + t_{S-1}) + beta C + bias over the tile's rows
+// and columns inside C, the segments' results added in segment order, each
+// step one FP32 operation (C not read when beta == 0).  ws holds S x nsplit
+// slots of th x 128 floats (rows of 128), slot seg * nsplit + i.  Workgroup
+// (i, y) takes rows 8y .. 8y+7 of split tile i, one 4-column group per
+// thread, so every load of the S segments is in flight at once (VEC:
+// 16-byte accesses to C and the bias; N % 4 == 0, C rows and bias 16-byte
 // aligned).
 // ---------------------------------------------------------------------------
+constexpr int RED_ROWS = 8;   // tile rows per reduction workgroup (256 threads)
+static_assert(RED_ROWS * (TILE / 4) == 256, "one 4-column group per thread");
+
 template <bool VEC>
-__global__ void ksplit_reduce_kernel(const float* __restrict__ ws, int S, int64_t M, int64_t N,
-                                     float alpha, float beta, float* C, int64_t ldc,
-                                     const float* __restrict__ bias)
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(
+    const float* __restrict__ ws, int S, int nsplit, int split_from, int tiles_n, int th, int64_t M,
+    int64_t N, float alpha, float beta, float* C, int64_t ldc, const float* __restrict__ bias)
 {
-    const int64_t groups = (N + 3) / 4;
-    const int64_t slice = M * N;
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= groups) return;
-    const int64_t j0 = g * 4;
-    for (int64_t i = blockIdx.y; i < M; i += gridDim.y) {
-        const float* w = ws + i * N + j0;
-        float* c = C + i * ldc + j0;
-        if (VEC) {
-            f32x4_t t = *reinterpret_cast<const f32x4_t*>(w);
-            for (int sg = 1; sg < S; ++sg) {
-                const f32x4_t u = *reinterpret_cast<const f32x4_t*>(w + sg * slice);
+    const int i = blockIdx.x;
+    const int tile = split_from + i;
+    const int tm = tile / tiles_n;
+    const int tn = tile - tm * tiles_n;
+    const int64_t m0 = (int64_t)tm * th, n0 = (int64_t)tn * TILE;
+    const int r = blockIdx.y * RED_ROWS + (int)(threadIdx.x / (TILE / 4));
+    const int cg = (int)(threadIdx.x % (TILE / 4)) * 4;
+    if (m0 + r >= M || n0 + cg >= N) return;
+    const int cols = N - n0 < TILE ? (int)(N - n0) : TILE;
+    const int64_t slot = (int64_t)th * TILE;
+    const int64_t seg_stride = (int64_t)nsplit * slot;
+    const float* w = ws + (int64_t)i * slot + (int64_t)r * TILE + cg;
+    float* c = C + (m0 + r) * ldc + n0 + cg;
+    if (VEC) {
+        f32x4_t t = *reinterpret_cast<const f32x4_t*>(w);
+        for (int sg = 1; sg < S; ++sg) {
+            const f32x4_t u = *reinterpret_cast<const f32x4_t*>(w + sg * seg_stride);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] = t[e] + u[e];
-            }
-            f32x4_t out;
+            for (int e = 0; e < 4; ++e) t[e] = t[e] + u[e];
+        }
+        f32x4_t out;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = alpha * t[e];
-            if (beta != 0.0f) {
-                const f32x4_t old = *reinterpret_cast<const f32x4_t*>(c);
+        for (int e = 0; e < 4; ++e) out[e] = alpha * t[e];
+        if (beta != 0.0f) {
+            const f32x4_t old = *reinterpret_cast<const f32x4_t*>(c);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(beta, old[e], out[e]);
-            }
-            if (bias != nullptr) {
-                const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(bias + j0);
+            for (int e = 0; e < 4; ++e) out[e] = __builtin_fmaf(beta, old[e], out[e]);
+        }
+        if (bias != nullptr) {
+            const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(bias + n0 + cg);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = out[e] + bv[e];
-            }
-            *reinterpret_cast<f32x4_t*>(c) = out;
-        } else {
-            for (int e = 0; e < 4 && j0 + e < N; ++e) {
-                float t = w[e];
-                for (int sg = 1; sg < S; ++sg) t = t + w[sg * slice + e];
-                float o = alpha * t;
-                if (beta != 0.0f) o = __builtin_fmaf(beta, c[e], o);
-                if (bias != nullptr) o = o + bias[j0 + e];
-                c[e] = o;
-            }
+            for (int e = 0; e < 4; ++e) out[e] = out[e] + bv[e];
+        }
+        *reinterpret_cast<f32x4_t*>(c) = out;
+    } else {
+        for (int e = 0; e < 4 && cg + e < cols; ++e) {
+            float t = w[e];
+            for (int sg = 1; sg < S; ++sg) t = t + w[sg * seg_stride + e];
+            float o = alpha * t;
+            if (beta != 0.0f) o = __builtin_fmaf(beta, c[e], o);
+            if (bias != nullptr) o = o + bias[n0 + cg + e];
+            c[e] = o;
         }
     }
 }
@@ -957,8 +994,9 @@ bool fused_a_path(const GemmArgs& g)
 
 namespace {
 
-// The workspace's parts: pre-split B (and A when not fused), then the split-K
-// partial results, each starting at a multiple of 256 bytes.
+// The workspace's parts: pre-split B (and A when not fused), then the split
+// tiles' partial results (ksplit slots of tile_m x 128 floats per split
+// tile), each starting at a multiple of 256 bytes.
 struct WsLayout {
     size_t b, a, c;   // offsets
     size_t total;
@@ -966,26 +1004,30 @@ struct WsLayout {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(const GemmArgs& g, int nbands, int ksplit)
+int effective_tile_m(const GemmArgs& g, int tile_m) { return fused_a_path(g) ? tile_m : TILE; }
+
+WsLayout ws_layout(const GemmArgs& g, int nbands, int ksplit, int tile_m, int64_t split_from)
 {
-    const int64_t tiles_m = (g.M + TILE - 1) / TILE;
+    tile_m = effective_tile_m(g, tile_m);
     const int64_t tiles_n = (g.N + TILE - 1) / TILE;
+    const int64_t ntiles = (g.M + tile_m - 1) / tile_m * tiles_n;
     const int64_t nk = (g.K + BK - 1) / BK;
     const int np = nbands >= 3 ? 3 : nbands;
     const bool fused = fused_a_path(g);
     WsLayout w;
     w.b = 0;
     w.a = g.Bplanes != nullptr ? 0 : round256((size_t)(tiles_n * nk * chunk_elems(np)) * sizeof(uint16_t));
-    w.c = w.a + (fused ? 0 : round256((size_t)(tiles_m * nk * chunk_elems(np)) * sizeof(uint16_t)));
-    w.total = w.c + (ksplit > 1 ? round256((size_t)ksplit * (size_t)g.M * (size_t)g.N * sizeof(float)) : 0);
+    w.c = w.a + (fused ? 0 : round256((size_t)((g.M + TILE - 1) / TILE * nk * chunk_elems(np)) * sizeof(uint16_t)));
+    const int64_t nsplit = ntiles - (split_from > 0 && split_from < ntiles ? split_from : 0);
+    w.total = w.c + (ksplit > 1 ? round256((size_t)ksplit * (size_t)nsplit * (size_t)tile_m * TILE * sizeof(float)) : 0);
     return w;
 }
 
 }  // namespace
 
-size_t gemm_bf16_workspace_bytes(const GemmArgs& g, int nbands, int ksplit)
+size_t gemm_bf16_workspace_bytes(const GemmArgs& g, int nbands, int ksplit, int tile_m, int64_t split_from)
 {
-    return ws_layout(g, nbands, ksplit).total;
+    return ws_layout(g, nbands, ksplit, tile_m, split_from).total;
 }
 
 size_t gemm_bf16_planes_bytes(int64_t N, int64_t K, int nbands)
@@ -1008,7 +1050,7 @@ hipError_t launch_presplit_b(const float* B, int64_t ldb, bool trans_b, int64_t 
                            planes, stream);
 }
 
-hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, int tile_m,
+hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, int64_t split_from, int tile_m,
                             const DeviceInfo& dev, void* workspace, hipStream_t stream)
 {
     if (nbands != 5 && nbands != 3 && nbands != 2 && nbands != 1) return hipErrorInvalidValue;
@@ -1017,14 +1059,22 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, int tile_
     if (!fused) tile_m = TILE;   // the pre-split kernel has 128-row tiles only
     const int64_t tiles_m = (g.M + tile_m - 1) / tile_m;
     const int64_t tiles_n = (g.N + TILE - 1) / TILE;
+    const int64_t ntiles = tiles_m * tiles_n;
     const int64_t nk = (g.K + BK - 1) / BK;
     const int64_t lim = (int64_t)1 << 31;
-    if (tiles_m * tiles_n >= lim || tiles_m * tiles_n * nk >= lim || tiles_n * nk >= lim ||
-        tiles_m * nk >= lim)
+    if (ntiles >= lim || ntiles * nk >= lim || tiles_n * nk >= lim || tiles_m * nk >= lim)
         return hipErrorInvalidValue;
-    const WsLayout lay = ws_layout(g, nbands, ksplit);
+    const int64_t grid_all = ntiles < dev.num_cu ? ntiles : dev.num_cu;
+    // a split of only the last round: whole rounds of whole tiles first, so
+    // split_from must be a positive multiple of the grid below ntiles (0:
+    // every tile split)
+    if (ksplit > 1 && split_from != 0 &&
+        (split_from < 0 || split_from >= ntiles || split_from % grid_all != 0))
+        return hipErrorInvalidValue;
+    if (ksplit <= 1) split_from = 0;
+    const WsLayout lay = ws_layout(g, nbands, ksplit, tile_m, split_from);
     if (ksplit < 1 || nk % ksplit != 0 || (ksplit > 1 && !fused) ||
-        tiles_m * tiles_n * ksplit >= lim || (workspace == nullptr && lay.total > 0) ||
+        split_from + (ntiles - split_from) * ksplit >= lim || (workspace == nullptr && lay.total > 0) ||
         ((uintptr_t)g.Bplanes & 15u) != 0)
         return hipErrorInvalidValue;
 
@@ -1042,17 +1092,18 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, int tile_
     p.beta = g.beta;
     p.bias = g.bias;
     p.tiles_n = (int)tiles_n;
-    p.ntiles = (int)(tiles_m * tiles_n);
+    p.ntiles = (int)ntiles;
     p.nk = (int)nk;
     p.ksplit = ksplit;
     p.nk_item = (int)(nk / ksplit);
+    p.split_from = (int)split_from;
     p.vec_a = fused ? 1 : 0;
     // (emulated kernels) C rows allow 16-byte stores at 16-byte aligned
     // columns, and the bias (if any) 16-byte loads there
     p.vec_b = (((uintptr_t)g.C & 15u) == 0 && (g.ldc & 3) == 0 &&
                (g.bias == nullptr || ((uintptr_t)g.bias & 15u) == 0) &&
                (int64_t)TILE * g.ldc * 4 < ((int64_t)1 << 31)) ? 1 : 0;
-    p.vec_ws = ((g.N & 3) == 0 && (int64_t)TILE * g.N * 4 < ((int64_t)1 << 31)) ? 1 : 0;
+    p.vec_ws = 1;   // slots of tile_m x 128 floats at 256-byte multiples: 16-byte rows
 
     const int np = nbands >= 3 ? 3 : nbands;
     char* ws = static_cast<char*>(workspace);
@@ -1068,7 +1119,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, int tile_
     if (e == hipSuccess && !fused)
         e = launch_presplit(np, g.A, g.lda, !g.trans_a, g.M, g.K, (int)tiles_m, (int)nk, Wa, stream);
     if (e == hipSuccess) {
-        const int64_t items = (int64_t)p.ntiles * ksplit;
+        const int64_t items = split_from + (ntiles - split_from) * ksplit;
         const int grid = items < dev.num_cu ? (int)items : dev.num_cu;
         switch (nbands) {
         case 5: e = launch_main<5>(p, fused, tile_m, grid, Wb, Wa, stream); break;
@@ -1078,17 +1129,18 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, int tile_
         }
     }
     if (e == hipSuccess && ksplit > 1) {
-        const int64_t groups = (g.N + 3) / 4;
-        const int bx = (int)((groups + 255) / 256);
-        const int by = (int)(g.M < 4096 ? g.M : 4096);
+        const int nsplit = (int)(ntiles - split_from);
         const bool vec = (g.N & 3) == 0 && ((uintptr_t)g.C & 15u) == 0 && (g.ldc & 3) == 0 &&
                          (g.bias == nullptr || ((uintptr_t)g.bias & 15u) == 0);
+        const dim3 rgrid(nsplit, tile_m / RED_ROWS);
         if (vec)
-            hipLaunchKernelGGL(ksplit_reduce_kernel<true>, dim3(bx, by), dim3(256), 0, stream, p.wsC,
-                               ksplit, g.M, g.N, g.alpha, g.beta, g.C, g.ldc, g.bias);
+            hipLaunchKernelGGL(ksplit_reduce_kernel<true>, rgrid, dim3(256), 0, stream, p.wsC, ksplit,
+                               nsplit, (int)split_from, (int)tiles_n, tile_m, g.M, g.N, g.alpha, g.beta,
+                               g.C, g.ldc, g.bias);
         else
-            hipLaunchKernelGGL(ksplit_reduce_kernel<false>, dim3(bx, by), dim3(256), 0, stream, p.wsC,
-                               ksplit, g.M, g.N, g.alpha, g.beta, g.C, g.ldc, g.bias);
+            hipLaunchKernelGGL(ksplit_reduce_kernel<false>, rgrid, dim3(256), 0, stream, p.wsC, ksplit,
+                               nsplit, (int)split_from, (int)tiles_n, tile_m, g.M, g.N, g.alpha, g.beta,
+                               g.C, g.ldc, g.bias);
         e = hipGetLastError();
     }
     return e;

@@ -307,8 +307,9 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_pp_kernel(Params p, const flo
     wc.tiles_n = p.tiles_n;
     wc.gtn = gtile % p.tiles_n;
     wc.gm = (int64_t)(gtile / p.tiles_n) * TILE;
-    wc.gseg = 0;
-    wc.mrows = (int64_t)(p.ntiles / p.tiles_n) * TILE;
+    wc.G = G;
+    wc.split_from = p.ntiles;
+    wc.nsplit = 1;
     wc.tail_k = (int)(p.K - (int64_t)(p.nk - 1) * BK);
     wc.M = p.M;
     wc.lda = p.lda;
@@ -466,11 +467,15 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_pp_kernel(Params p, const flo
     wm.tn = slot % p.tiles_n;
     wm.m0 = (int64_t)(slot / p.tiles_n) * TILE;
     wm.left = my_items - 1;
-    walk_start_segment(wm, wc);
+    wm.kt = 0;
+    wm.kt_end = p.nk;
+    wm.item = slot;
+    wm.part = 0;
+    wm.widx = 0;
     walk_set_tile(wm, wc);
     wm.kvalid = wm.kt + 1 < p.nk ? BK : wc.tail_k;
     Walk ws = wm, wa = wm;
-    TilePos we{wm.m0, wm.tn, wm.rows, wm.seg};
+    TilePos we{wm.m0, wm.tn, wm.rows, wm.seg, 0, 0};
     // Prologue: B chunk of step 0 (each group its half) and group 1's half
     // of chunk 1; A rows of steps 0 and 1 (stages 0 and 1).
     copy_b_half(ws, 0);
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_pp_kernel(Params p, const flo
             __builtin_amdgcn_sched_barrier(0);
         }
         epi = wm.kt == p.nk - 1;
-        we = TilePos{wm.m0, wm.tn, wm.rows, wm.seg};
+        we = TilePos{wm.m0, wm.tn, wm.rows, wm.seg, wm.part, wm.widx};
         wm = ws;
         ws = wa;
         walk_next<false>(wa, wc);

@@ -40,11 +40,15 @@ bool fused_a_path(const GemmArgs& g);
 // Device workspace the emulated path needs (bytes, a multiple of 256), and
 // the launch with it: nbands 5 (BF16X9), 3 (BF16X6), 2 (BF16X3) or 1
 // (BF16X1); ksplit K segments, a divisor of ceil(K / 32), 1 unless
-// fused_a_path(g); tile_m the rows of an output tile, 128 or 64 (64 only
-// on the fused path, otherwise 128 is used; the result does not depend on
-// it); `workspace` 256-byte aligned, used in stream order only.
-size_t gemm_bf16_workspace_bytes(const GemmArgs& g, int nbands, int ksplit);
-hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, int tile_m,
+// fused_a_path(g), for the output tiles from split_from on (0: all; else a
+// positive multiple of min(tiles, CUs) below the tile count: whole rounds
+// of whole tiles, then the last round's tiles split); tile_m the rows of an output tile, 128 or 64 (64 only on the fused
+// path, otherwise 128 is used; the result does not depend on it; the tiles
+// split_from counts are of that height); `workspace` 256-byte aligned,
+// used in stream order only.
+size_t gemm_bf16_workspace_bytes(const GemmArgs& g, int nbands, int ksplit, int tile_m,
+                                 int64_t split_from);
+hipError_t launch_gemm_bf16(const GemmArgs& g, int nbands, int ksplit, int64_t split_from, int tile_m,
                             const DeviceInfo& dev, void* workspace, hipStream_t stream);
 // The native FP32 GEMM: its device workspace (bytes, a multiple of 256; 0
 // when the call takes the kernel that needs none) and the launch with it

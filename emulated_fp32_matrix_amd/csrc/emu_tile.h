@@ -29,10 +29,13 @@ struct Params {
     // with the 16-byte epilogue: C rows (and the bias) allow 16-byte access
     int vec_b;
     // Split of K into ksplit equal segments of nk_item k-steps (fused-A
-    // kernel only; 1: none).  With ksplit > 1 the kernel writes each
-    // (segment, tile) result t, unscaled, to wsC[seg][M][N] (vec_ws: 16-byte
-    // stores allowed there) and a reduction kernel forms C.
-    int ksplit, nk_item;
+    // kernel only; 1: none), for the tiles from split_from on (0: every
+    // tile; otherwise a multiple of the grid: whole rounds of whole tiles
+    // first).  With ksplit > 1 the kernel writes each (segment, split tile)
+    // result t, unscaled, to its slot of wsC (tile_m x 128 floats, slot
+    // seg * (ntiles - split_from) + tile - split_from; vec_ws: 16-byte stores
+    // allowed there) and a reduction kernel forms C on those tiles.
+    int ksplit, nk_item, split_from;
     float* wsC;
     int vec_ws;
 };

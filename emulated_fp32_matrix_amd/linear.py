@@ -36,7 +36,7 @@ import math
 
 import torch
 
-from . import presplit_b, select_ksplit, select_mode, sgemm, sgemm_presplit
+from . import KSPLIT_AUTO, presplit_b, select_mode, sgemm, sgemm_presplit
 
 _EMULATED = ("BF16X9", "BF16X6", "BF16X3", "BF16X1")
 
@@ -60,8 +60,8 @@ class _PlanesCache:
 def _gemm(a, w, trans_b, mode, bias, cache):
     """a @ op(w) (+ bias) in `mode`; with a cache and an emulated mode (the
     one AUTO would run, when mode is AUTO) through the weight's planes, with
-    the K split the library would choose itself, so the result is the same
-    bit for bit."""
+    the K split plan the library would choose itself, so the result is the
+    same bit for bit."""
     if cache is None:
         return sgemm(a, w, mode=mode, trans_b=trans_b, bias=bias)
     M, K = a.shape
@@ -69,10 +69,9 @@ def _gemm(a, w, trans_b, mode, bias, cache):
     run = select_mode(M, N, K) if mode == "AUTO" else mode
     if run not in _EMULATED:
         return sgemm(a, w, mode=run, trans_b=trans_b, bias=bias)
-    # the library splits K only under AUTO and only where A is split inside
-    # the GEMM (k-contiguous rows, 16-byte aligned, K a multiple of 4)
-    fused = a.data_ptr() % 16 == 0 and K % 4 == 0 and a.stride(0) % 4 == 0
-    ksplit = select_ksplit(M, N, K) if mode == "AUTO" and fused else 1
+    # the library splits K only under AUTO (KSPLIT_AUTO: its plan in the
+    # mode AUTO runs) and only where A is split inside the GEMM
+    ksplit = KSPLIT_AUTO if mode == "AUTO" else 1
     return sgemm_presplit(a, cache.get(w, run), bias=bias, ksplit=ksplit)
 
 

@@ -16,9 +16,11 @@ Per stack and policy it reports the step time two ways:
            device work alone (what a captured graph or a busy stream sees).
 
 With --ksplit-sweep it instead times every GEMM of the stacks in BF16X9
-with each K split S (a divisor of ceil(K/32), S <= 8; emu_sgemm_ex), beside
-the split the AUTO policy picks (emu_sgemm_ksplit) and native FP32 (device
-time, calls queued behind a GPU spin, median of 5 runs of 20 calls).
+with each K split S of every tile (a divisor of ceil(K/32), S <= 8;
+emu_sgemm_ex), beside the plan the AUTO policy picks (emu_sgemm_plan: a split
+of every tile, of the last round of tiles only, or none; run in BF16X9 with
+EMU_KSPLIT_AUTO) and native FP32 (device time, calls queued behind a GPU
+spin, median of 5 runs of 20 calls).
 
     python3 -m emulated_fp32_matrix_amd.policies [--stacks 2 3 4] [--json out.json]
     python3 -m emulated_fp32_matrix_amd.policies --ksplit-sweep --stacks 2 4 [--json out.json]
@@ -62,7 +64,7 @@ def time_stack(stack, reps=5):
     flops = sum(g.flops for g in gemms)
     choice = {g.name: emu.select_mode(g.M, g.N, g.K, g.trans_a, g.trans_b) for g in gemms}
 
-    splits = {g.name: emu.select_ksplit(g.M, g.N, g.K) for g in gemms}
+    plans = {g.name: emu.select_plan(g.M, g.N, g.K) for g in gemms}
     # "AUTO+planes": AUTO's choices with the weights split once beforehand
     # (emu_presplit_b, outside the timed region) and emu_sgemm_presplit
     planes = {g.name: emu.presplit_b(b, mode="BF16X9", trans_b=g.trans_b)
@@ -71,13 +73,13 @@ def time_stack(stack, reps=5):
     def step(mode):
         for g, a, b, c in tensors:
             if mode == "AUTO+planes" and g.name in planes:
-                emu.sgemm_presplit(a, planes[g.name], trans_a=g.trans_a, c=c, ksplit=splits[g.name])
+                emu.sgemm_presplit(a, planes[g.name], trans_a=g.trans_a, c=c, ksplit=emu.KSPLIT_AUTO)
             else:
                 emu.sgemm(a, b, mode="AUTO" if mode == "AUTO+planes" else mode, trans_a=g.trans_a,
                           trans_b=g.trans_b, c=c)
 
     out = {"stack": stack, "name": synth.CONFIG_NAMES[stack], "gflop": flops / 1e9,
-           "auto_choice": choice, "auto_ksplit": splits, "policies": {}}
+           "auto_choice": choice, "auto_plan": plans, "policies": {}}
     for pol, mode in POLICIES.items():
         for _ in range(3):
             step(mode)
@@ -145,12 +147,16 @@ def ksplit_sweep(stack):
                                                     trans_b=g.trans_b, c=c, ksplit=S))
         native = _device_us(lambda: emu.sgemm(a, b, mode="NATIVE_F32", trans_a=g.trans_a,
                                               trans_b=g.trans_b, c=c))
-        auto = emu.select_ksplit(g.M, g.N, g.K)
+        plan = emu.select_plan(g.M, g.N, g.K)
+        auto_us = _device_us(lambda: emu.sgemm(a, b, mode="BF16X9", trans_a=g.trans_a,
+                                               trans_b=g.trans_b, c=c, ksplit=emu.KSPLIT_AUTO))
         best = min(times, key=times.get)
-        rows.append({"gemm": g.name, "M": g.M, "N": g.N, "K": g.K, "auto_ksplit": auto,
-                     "best_ksplit": best, "x9_us": {str(k): round(v, 1) for k, v in times.items()},
+        rows.append({"gemm": g.name, "M": g.M, "N": g.N, "K": g.K, "auto_plan": list(plan),
+                     "auto_us": round(auto_us, 1), "best_ksplit": best,
+                     "x9_us": {str(k): round(v, 1) for k, v in times.items()},
                      "native_us": round(native, 1)})
-        print(f"stack {stack} {g.name:8s} {g.M}x{g.N}x{g.K}: auto S={auto} best S={best}  " +
+        print(f"stack {stack} {g.name:8s} {g.M}x{g.N}x{g.K}: auto plan {plan} {auto_us:6.1f} us, "
+              f"best full split S={best}  " +
               "  ".join(f"S{k} {v:6.1f}" for k, v in times.items()) + f"  native {native:6.1f} us",
               flush=True)
         del a, b, c
@@ -162,8 +168,8 @@ def _policy_markdown(res):
     out = []
     for r in res:
         out.append(f"## Stack: {r['name']} ({r['gflop']:.2f} GFLOP per step)\n")
-        choice = ", ".join(f"{k} {v}" + (f" (K split {r['auto_ksplit'][k]})"
-                                          if r.get("auto_ksplit", {}).get(k, 1) > 1 else "")
+        choice = ", ".join(f"{k} {v}" + (f" ({_plan_text(r['auto_plan'][k])})"
+                                          if v != "NATIVE_F32" and r["auto_plan"][k][0] > 1 else "")
                            for k, v in r["auto_choice"].items())
         out.append(f"AUTO's choices: {choice}\n")
         out.append("| policy | mode | wall us | wall TFLOP/s | wall speedup | device us | device TFLOP/s "
@@ -177,29 +183,39 @@ def _policy_markdown(res):
     return "\n".join(out)
 
 
+def _plan_text(plan):
+    """'S = 2 on the last round (tiles 256..383 of 384, 128 rows)' and the like."""
+    S, th, sf = plan
+    if S == 1:
+        return f"no split, {th}-row tiles"
+    if sf == 0:
+        return f"S = {S} on every tile, {th}-row tiles"
+    return f"S = {S} on the tiles from {sf} on, {th}-row tiles"
+
+
 def _ksplit_markdown(res):
     out = []
     for r in res:
         splits = sorted({int(s) for g in r["gemms"] for s in g["x9_us"]})
         out.append(f"## {r['name']}\n")
-        out.append("| GEMM | M x N x K | tiles | " + " | ".join(f"S = {s}" for s in splits) +
-                   " | native | AUTO S | best S | AUTO vs S = 1 |")
-        out.append("|---|---|---|" + "---|" * len(splits) + "---|---|---|---|")
+        out.append("| GEMM | M x N x K | 128-row tiles | " + " | ".join(f"S = {s}" for s in splits) +
+                   " | native | AUTO plan | AUTO plan us | best full split | AUTO vs S = 1 |")
+        out.append("|---|---|---|" + "---|" * len(splits) + "---|---|---|---|---|")
         tot = {"s1": 0.0, "auto": 0.0, "best": 0.0, "native": 0.0}
         for g in r["gemms"]:
             t = {int(k): v for k, v in g["x9_us"].items()}
             tiles = -(-g["M"] // 128) * -(-g["N"] // 128)
             cells = " | ".join(f"{t[s]:.1f}" if s in t else "" for s in splits)
-            auto = t[g["auto_ksplit"]]
+            auto = g["auto_us"]
             out.append(f"| {g['gemm']} | {g['M']} x {g['N']} x {g['K']} | {tiles} | {cells} | "
-                       f"{g['native_us']:.1f} | {g['auto_ksplit']} | {g['best_ksplit']} | "
-                       f"{t[1] / auto:.2f}x |")
+                       f"{g['native_us']:.1f} | {_plan_text(g['auto_plan'])} | {auto:.1f} | "
+                       f"S = {g['best_ksplit']} | {t[1] / auto:.2f}x |")
             tot["s1"] += t[1]
             tot["auto"] += auto
             tot["best"] += t[g["best_ksplit"]]
             tot["native"] += g["native_us"]
-        out.append(f"\nStack total: S = 1 {tot['s1']:.1f} us, AUTO's split {tot['auto']:.1f} us "
-                   f"({tot['s1'] / tot['auto']:.2f}x), best split {tot['best']:.1f} us, "
+        out.append(f"\nStack total: S = 1 {tot['s1']:.1f} us, AUTO's plan {tot['auto']:.1f} us "
+                   f"({tot['s1'] / tot['auto']:.2f}x), best full split per GEMM {tot['best']:.1f} us, "
                    f"native {tot['native']:.1f} us.\n")
     return "\n".join(out)
 

@@ -30,8 +30,9 @@
  *     or K not a multiple of 4, and the partial results of a split K).  Size
  *     for B: planes * 2 bytes * ceil(N/128)*128 * ceil(K/32)*32 (3 planes,
  *     2 in BF16X3, 1 in BF16X1),
- *     likewise with M for A; S * M * N * 4 bytes for a split into S
- *     segments.  NATIVE_F32 needs one for op(B) packed as FP32, 4 bytes *
+ *     likewise with M for A; S * T * R * 128 * 4 bytes for a split into S
+ *     segments of T output tiles of R rows (every tile: T * R * 128 is
+ *     about M * N; emu_sgemm_plan gives T and R of the automatic plan).  NATIVE_F32 needs one for op(B) packed as FP32, 4 bytes *
  *     ceil(N/128)*128 * ceil(K/32)*32, when A is k-contiguous and 16-byte
  *     addressable (transA == N, A 16-byte aligned, lda and K multiples of
  *     4), and none otherwise.  The library keeps one workspace per (device, stream): a
@@ -102,6 +103,11 @@ typedef enum {
 /* Bytes of the fixed per-device scratch emu_sgemm_noalloc works in. */
 #define EMU_NOALLOC_SCRATCH_BYTES (64ull << 20)
 
+/* ksplit of emu_sgemm_ex, emu_sgemm_noalloc and emu_sgemm_presplit: the
+ * plan EMU_MODE_AUTO uses for the shape (emu_sgemm_plan), in the explicit
+ * emulated mode given.  (ABI 1.7) */
+#define EMU_KSPLIT_AUTO (-1)
+
 /*
  * C = alpha * op(A) . op(B) + beta * C in FP32, computed in `mode`.
  *
@@ -113,8 +119,8 @@ typedef enum {
  * or 1) are recombined smallest first, t = S_{n-1}, t = S_j + 2^-8 t, and then
  * C = alpha * t + beta * C.  In EMU_MODE_AUTO the library chooses, per shape,
  * the mode (emu_sgemm_select) and, for an emulated mode, possibly a split of
- * K into segments (emu_sgemm_ksplit, emu_sgemm_ex): then t is the sum, in
- * segment order, of the segments' t.  So in AUTO a row of C may differ in its
+ * K into segments on some or all output tiles (emu_sgemm_plan, emu_sgemm_ex):
+ * there t is the sum, in segment order, of the segments' t.  So in AUTO a row of C may differ in its
  * last bits between shapes; in an explicit mode it never depends on the
  * other rows.  Every result is deterministic for a given shape.
  *
@@ -167,25 +173,33 @@ emu_status_t emu_sgemm_bias(emu_op_t transA, emu_op_t transB, int64_t M, int64_t
  * Performance for Machine Learning Interatomic Potentials", section "BF16x9
  * on NVIDIA Blackwell GPUs" (Figures 3 and 4: the smallest GEMM and MD-step
  * speedups), have fewer 128 x 128 output tiles than the device has compute
- * units.  Splitting K runs several K segments of each tile at once.  The
- * split is this library's, not the pages'.
+ * units, and others leave the last round of tiles over the compute units
+ * partly filled.  Splitting K runs several K segments of a tile at once.
+ * The split is this library's, not the pages'.
  *
  *   ksplit = 0:  as emu_sgemm_bias: with EMU_MODE_AUTO the performant policy
- *                splits where its cost model predicts a gain (the split
- *                emu_sgemm_ksplit reports); an explicit mode does not split;
- *   ksplit >= 1: exactly that many segments; it must divide n = ceil(K / 32)
- *                and needs an explicit emulated mode (BF16X9, X6, X3, X1).
+ *                splits where its cost model predicts a gain (the plan
+ *                emu_sgemm_plan reports); an explicit mode does not split;
+ *   ksplit = EMU_KSPLIT_AUTO (-1): that policy's plan in an explicit
+ *                emulated mode (no split where A does not allow one, see
+ *                below): the result equals EMU_MODE_AUTO's bit for bit when
+ *                AUTO runs that mode;
+ *   ksplit >= 1: exactly that many segments on every output tile; it must
+ *                divide n = ceil(K / 32) and needs an explicit emulated mode
+ *                (BF16X9, X6, X3, X1).
  *
  * With S segments, segment s covers the k-steps [s n / S, (s + 1) n / S) of
- * 32 k each.  Each segment's product t_s is formed as without a split (band
- * accumulation, recombination), and then
+ * 32 k each.  On a split tile each segment's product t_s is formed as
+ * without a split (band accumulation, recombination), and then
  *     C = alpha (t_0 + t_1 + ... + t_{S-1}) + beta C + bias,
- * summed in segment order, every operation one FP32 rounding.  The result is
- * a deterministic function of (inputs, ksplit): it does not depend on
- * timing.  S > 1 adds S x M x N floats to the workspace.
+ * summed in segment order, every operation one FP32 rounding; elements of a
+ * tile that is not split are those of the call without a split.  The result
+ * is a deterministic function of (inputs, ksplit) (and, for the automatic
+ * plan, the shape): it does not depend on timing.  The split adds S floats
+ * per element of the split tiles to the workspace.
  *
- * Errors: as emu_sgemm_bias; EMU_STATUS_INVALID_VALUE for ksplit < 0, for
- * ksplit > 0 with EMU_MODE_NATIVE_F32 or EMU_MODE_AUTO, or for ksplit > 1
+ * Errors: as emu_sgemm_bias; EMU_STATUS_INVALID_VALUE for ksplit < -1, for
+ * ksplit != 0 with EMU_MODE_NATIVE_F32 or EMU_MODE_AUTO, or for ksplit > 1
  * that does not divide ceil(K / 32) (or K = 0); EMU_STATUS_NOT_SUPPORTED for
  * ksplit > 1 when op(A) is transposed or A is not 16-byte addressable (A
  * 16-byte aligned, lda and K multiples of 4): that path splits A into BF16
@@ -218,7 +232,7 @@ emu_status_t emu_sgemm_ex(emu_op_t transA, emu_op_t transB, int64_t M, int64_t N
  *
  * Errors: as emu_sgemm_ex; also EMU_STATUS_SCRATCH_TOO_SMALL, before any
  * launch, when the call needs more than EMU_NOALLOC_SCRATCH_BYTES (for
- * example a split K of S * M * N * 4 bytes beyond it), and
+ * example a split K of about S * M * N * 4 bytes beyond it), and
  * EMU_STATUS_INTERNAL if the scratch's address could not be resolved.
  * (ABI 1.6)
  */
@@ -228,12 +242,29 @@ emu_status_t emu_sgemm_noalloc(emu_op_t transA, emu_op_t transB, int64_t M, int6
                                int ksplit, void* stream);
 
 /*
- * The K split EMU_MODE_AUTO uses for this shape when it runs the emulation and
- * A allows a split (see emu_sgemm_ex); a caller of an explicit emulated mode
- * may pass it to emu_sgemm_ex.  It is the divisor S <= 8 of ceil(K / 32)
- * with the least time under the library's cost model, and 1 unless that
- * saves at least 5 %.  A pure host function of (M, N, K): deterministic, no
- * device access.
+ * The plan of the emulated kernel EMU_MODE_AUTO uses for this shape when it
+ * runs the emulation and A allows a split (see emu_sgemm_ex); a caller of
+ * an explicit emulated mode gets it with ksplit = EMU_KSPLIT_AUTO.  Output
+ * tiles are tile_rows x 128 (tile_rows 128 or 64), numbered row by row,
+ * columns fastest: tile i covers rows (i / ceil(N/128)) * tile_rows and
+ * columns (i % ceil(N/128)) * 128 onwards.  The tiles from split_from on
+ * have their K split into ksplit segments (emu_sgemm_ex); ksplit == 1 (no
+ * split) reports split_from = the tile count, and split_from == 0 means
+ * every tile.  A split of only some tiles takes whole rounds of 256 tiles
+ * (one per compute unit) unsplit and splits the last, partly filled round.
+ * The plan is the fastest under the library's cost model of: no split; for
+ * each divisor S <= 8 of ceil(K / 32), every tile split; and the last round
+ * split; and no split unless a split saves at least 5 %.  On a device
+ * with another number of compute units than 256, a plan that splits the
+ * last round only runs as a split of every tile (the same S).  A pure host
+ * function of (M, N, K): deterministic, no device access.  (ABI 1.7)
+ * Errors: EMU_STATUS_INVALID_VALUE for negative dimensions or a NULL pointer.
+ */
+emu_status_t emu_sgemm_plan(int64_t M, int64_t N, int64_t K, int* ksplit, int* tile_rows,
+                            int64_t* split_from);
+
+/*
+ * The ksplit of emu_sgemm_plan alone.
  * Errors: EMU_STATUS_INVALID_VALUE for negative dimensions or a NULL ksplit.
  */
 emu_status_t emu_sgemm_ksplit(int64_t M, int64_t N, int64_t K, int* ksplit);
@@ -276,8 +307,8 @@ emu_status_t emu_presplit_b(emu_op_t transB, int64_t N, int64_t K, const float* 
  * emu_sgemm_presplit: as emu_sgemm_ex, with op(B) given by planes that
  * emu_presplit_b wrote for the same N, K and mode (a mismatch is not
  * detected: the caller keeps them together).  `mode` must be one of the
- * four emulated modes; ksplit 0 or 1 is no split, S > 1 as in emu_sgemm_ex
- * (emu_sgemm_ksplit gives the split EMU_MODE_AUTO would use).
+ * four emulated modes; ksplit 0 or 1 is no split, S > 1 and
+ * EMU_KSPLIT_AUTO (the plan EMU_MODE_AUTO would use) as in emu_sgemm_ex.
  * Errors: as emu_sgemm_ex (without the op(B) checks); also
  * EMU_STATUS_INVALID_VALUE for NATIVE_F32 or AUTO, or (M, N, K > 0) NULL or
  * non-16-byte-aligned planes.
@@ -316,12 +347,13 @@ emu_status_t emu_sgemm_select(emu_op_t transA, emu_op_t transB, int64_t M, int64
  * codes give "EMU_STATUS_UNKNOWN".  Never NULL. */
 const char* emu_status_string(emu_status_t status);
 
-/* ABI version of this header (major * 100 + minor): 106 (1.1 added
+/* ABI version of this header (major * 100 + minor): 107 (1.1 added
  * emu_sgemm_bias, 1.2 EMU_MODE_BF16X1, 1.3 emu_sgemm_ex and
  * emu_sgemm_ksplit, 1.4 emu_presplit_b_bytes, emu_presplit_b and
  * emu_sgemm_presplit, 1.5 a stream workspace for NATIVE_F32, which may
  * therefore return EMU_STATUS_ALLOC_FAILED, 1.6 emu_sgemm_noalloc and
- * EMU_STATUS_SCRATCH_TOO_SMALL). */
+ * EMU_STATUS_SCRATCH_TOO_SMALL, 1.7 emu_sgemm_plan, EMU_KSPLIT_AUTO and
+ * AUTO plans that split the K of the last round of tiles only). */
 int emu_abi_version(void);
 
 #ifdef __cplusplus

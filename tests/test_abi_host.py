@@ -48,7 +48,7 @@ def test_status_strings_and_version():
     assert emu.emu_status_string(5) == "EMU_STATUS_INTERNAL"
     assert emu.emu_status_string(6) == "EMU_STATUS_SCRATCH_TOO_SMALL"
     assert emu.emu_status_string(99) == "EMU_STATUS_UNKNOWN"
-    assert emu.emu_abi_version() == 106
+    assert emu.emu_abi_version() == 107
 
 
 def test_noalloc_scratch_size_matches_header():
@@ -101,9 +101,11 @@ def test_bias_entry_point_invalid_arguments_rejected(args):
 
 
 @pytest.mark.parametrize("args", [
-    dict(ksplit=-1),
+    dict(ksplit=-2),
     dict(ksplit=2, mode=0),     # a split needs an emulated mode: not NATIVE_F32
     dict(ksplit=2, mode=4),     # nor AUTO
+    dict(ksplit=-1, mode=0),    # EMU_KSPLIT_AUTO too
+    dict(ksplit=-1, mode=4),
     dict(ksplit=1, mode=0),
     dict(ksplit=3),             # K = 64: 2 k-steps, 3 does not divide them
     dict(ksplit=4),
@@ -155,7 +157,7 @@ def test_presplit_invalid_arguments_rejected(args):
 @pytest.mark.parametrize("args", [
     dict(mode="NATIVE_F32"), dict(mode="AUTO"), dict(planes=0), dict(planes=FAKE + 8),
     dict(transA=2), dict(M=-1), dict(lda=63), dict(C=0), dict(A=0), dict(ldc=5),
-    dict(ksplit=-1), dict(ksplit=3),   # K = 64: 2 k-steps, 3 does not divide them
+    dict(ksplit=-2), dict(ksplit=3),   # K = 64: 2 k-steps, 3 does not divide them
 ])
 def test_sgemm_presplit_invalid_arguments_rejected(args):
     call = dict(transA=0, M=10, N=6, K=64, alpha=1.0, A=FAKE, lda=64, planes=FAKE, beta=0.0, C=FAKE,
@@ -183,6 +185,45 @@ def test_ksplit_choice_is_pure_and_follows_the_cost_model():
         nk = -(-K // 32)
         assert 1 < S <= 8 and nk % S == 0, (M, N, K, S)
         assert all(emu.select_ksplit(M, N, K) == S for _ in range(3))
+
+
+def _plan_ok(M, N, K, plan):
+    S, th, sf = plan
+    tiles = -(-M // th) * -(-N // 128)
+    nk = -(-K // 32)
+    assert th in (64, 128) and 1 <= S <= 8, plan
+    if S == 1:
+        assert sf == tiles, plan
+    else:
+        assert nk % S == 0, plan
+        assert sf == 0 or (0 < sf < tiles and sf % 256 == 0), plan
+
+
+def test_plan_is_pure_and_consistent():
+    """emu_sgemm_plan: no device access, deterministic, its ksplit that of
+    emu_sgemm_ksplit; split_from is the tile count without a split, else 0
+    or whole rounds of 256 tiles below the tile count."""
+    assert emu.emu_sgemm_plan(-1, 4, 4)[0] == emu.STATUS_INVALID_VALUE
+    assert emu._lib.emu_sgemm_plan(4, 4, 4, None, None, None) == emu.STATUS_INVALID_VALUE
+    assert emu.select_plan(0, 5, 5)[0] == 1
+    shapes = [(552960, 768, 256), (552960, 256, 768), (6144, 768, 256), (6144, 256, 768),
+              (6144, 3072, 1024), (6144, 1024, 1024), (6144, 1024, 4096), (6144, 4096, 1024),
+              (2048, 2048, 2048), (256, 256, 256), (512, 256, 4096), (333, 777, 1000),
+              (4096, 4096, 4096), (1, 1, 1)]
+    for M, N, K in shapes:
+        plan = emu.select_plan(M, N, K)
+        _plan_ok(M, N, K, plan)
+        assert plan[0] == emu.select_ksplit(M, N, K)
+        assert all(emu.select_plan(M, N, K) == plan for _ in range(3))
+
+
+def test_plan_splits_the_last_round_of_tiles():
+    """At 6,144 rows and d = 1024 the 128 x 128 tiles fill whole rounds of
+    256 and leave part of one: the plan splits that round only."""
+    for M, N, K in [(6144, 1024, 1024), (6144, 3072, 1024), (6144, 1024, 3072)]:
+        S, th, sf = emu.select_plan(M, N, K)
+        tiles = -(-M // th) * -(-N // 128)
+        assert S > 1 and 0 < sf < tiles and sf % 256 == 0, (M, N, K, S, th, sf)
 
 
 def test_empty_shapes_return_before_touching_the_device():

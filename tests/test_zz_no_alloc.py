@@ -37,6 +37,8 @@ CASES = [
      (200, 100, 36, False, False, "NATIVE_F32", 0, True, 1.0, 0.0)),
     ((6144, 768, 256, False, False, "AUTO", 0, False, 1.0, 0.0),
      (6144, 256, 768, False, True, "AUTO", 0, True, 1.0, 0.0)),
+    ((6144, 1024, 1024, False, False, "AUTO", 0, True, 1.0, 0.0),   # last round of tiles split
+     (3300, 1200, 512, False, True, "BF16X6", -1, True, 0.5, 2.0)),
 ]
 
 
