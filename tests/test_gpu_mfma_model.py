@@ -21,6 +21,7 @@ import pytest
 
 import oracle
 from gpu_helpers import run, say
+from mfma_families import FAMILIES, family as _family
 from mfma_vectors import VECTORS
 
 pytestmark = pytest.mark.gpu
@@ -63,54 +64,12 @@ def test_hand_worked_instructions_on_the_matrix_unit():
         assert out16[j].view(np.uint32) == np.float32(VECTORS[i][4]).view(np.uint32), VECTORS[i][0]
 
 
-def _bf16(rng, shape, lo, hi):
-    m = rng.integers(128, 256, shape) * rng.choice([-1, 1], shape)
-    return (m * 2.0 ** (rng.integers(lo, hi, shape) - 7)).astype(np.float32)
-
-
-def _family(name, rng, M, N):
-    """Operands A (M x 32), B (32 x N), all exact BF16 numbers."""
-    if name == "wide exponents":
-        a, b = _bf16(rng, (M, 32), -30, 30), _bf16(rng, (32, N), -30, 30)
-        a[rng.random((M, 32)) < 0.15] = 0.0
-    elif name == "cancellation":
-        # the second instruction's products nearly cancel the first's sum:
-        # a_k negated, b_k one BF16 unit (of 2^-7 relative) off or equal
-        a, b = _bf16(rng, (M, 32), -4, 4), _bf16(rng, (32, N), -4, 4)
-        a[:, 16:24] = -a[:, 0:8]
-        m = rng.integers(129, 255, (8, N)) * rng.choice([-1, 1], (8, N))
-        e = rng.integers(-4, 4, (8, N)) - 7
-        b[0:8, :] = (m * 2.0**e).astype(np.float32)
-        b[16:24, :] = ((m + rng.integers(-1, 2, (8, N))) * 2.0**e).astype(np.float32)
-    elif name == "binade edges":
-        # accumulators just below and at powers of two, small second products
-        a = np.zeros((M, 32), np.float32)
-        b = np.zeros((32, N), np.float32)
-        a[:, 0] = 2.0 ** rng.integers(-3, 4, M)
-        b[0, :] = 1.0
-        a[:, 1] = -(2.0 ** rng.integers(-30, -20, M))
-        b[1, :] = rng.choice([0.0, 1.0, 2.0, 4.0], N)
-        a[:, 16:] = _bf16(rng, (M, 16), -26, -10)
-        b[16:, :] = _bf16(rng, (16, N), -6, 6)
-    elif name == "ties":
-        # products of 1.5 x 2^-12 style operands land on half-units of the grid
-        a = (1.5 * 2.0 ** rng.integers(-14, -9, (M, 32)) * rng.choice([-1, 1], (M, 32))).astype(np.float32)
-        b = (2.0 ** rng.integers(-14, -9, (32, N)) * rng.choice([-1, 1], (32, N))).astype(np.float32)
-        a[:, 0] = 1.0
-        b[0, :] = rng.choice([1.0, -1.0, 2.0], N)
-        a[:, 16] = 1.0
-        b[16, :] = rng.choice([0.0, 1.0], N)
-    else:
-        raise ValueError(name)
-    return a, b
-
-
-@pytest.mark.parametrize("family", ["wide exponents", "cancellation", "binade edges", "ties"])
+@pytest.mark.parametrize("family", FAMILIES)
 def test_random_instruction_pairs_match_the_model(family):
     """256 x 256 entries per family, each two instructions on the matrix
     unit, against the model applied twice (oracle.mfma_bf16_dot16), bit for
     bit."""
-    rng = np.random.default_rng(["wide exponents", "cancellation", "binade edges", "ties"].index(family))
+    rng = np.random.default_rng(FAMILIES.index(family))
     M = N = 256
     a, b = _family(family, rng, M, N)
     out = run(a, b, "BF16X1")
@@ -124,3 +83,31 @@ def test_random_instruction_pairs_match_the_model(family):
     say(f"{family}: {M * N} instruction pairs, {int(diff.sum())} differ from the model")
     assert not diff.any(), (f"{family}: {int(diff.sum())} entries differ, e.g. gpu "
                             f"{out[diff][:3]} model {want[diff][:3]}")
+
+
+def test_each_rule_of_the_model_is_necessary():
+    """The search of "Accurate Models of NVIDIA Tensor Cores" run on the
+    hardware: for every family, 1,024 sampled instruction pairs of a 128 x
+    128 GEMM in BF16X1 against each rule variant of tests/mfma_search.py.
+    The model's rules (the default) match every sample; each alternative
+    misses at least one sample over the families."""
+    import mfma_search as ms
+
+    M = N = 128
+    miss = {name: 0 for name, _ in [("default", ms.DEFAULT)] + ms.ALTERNATIVES}
+    for fi, fam in enumerate(FAMILIES):
+        rng = np.random.default_rng(200 + fi)
+        a, b = _family(fam, rng, M, N)
+        out = run(a, b, "BF16X1").view(np.uint32)
+        ab, bb = _bf16_bits(a), _bf16_bits(b)
+        pick = np.random.default_rng(300 + fi).choice(M * N, 1024, replace=False)
+        for name, r in [("default", ms.DEFAULT)] + ms.ALTERNATIVES:
+            got = np.array([ms.instruction_pair(ab[k // N], bb[:, k % N], r) for k in pick],
+                           np.float32).view(np.uint32)
+            miss[name] += int((got != out.reshape(-1)[pick]).sum())
+        say(f"{fam}: searched 1024 instruction pairs")
+    for name, n in miss.items():
+        say(f"  {name:40s} {n:5d} of {1024 * len(FAMILIES)} differ from the GPU")
+    assert miss["default"] == 0, "the model's own rules differ from the hardware"
+    survivors = [name for name, n in miss.items() if name != "default" and n == 0]
+    assert not survivors, f"alternatives the hardware does not contradict: {survivors}"

@@ -219,3 +219,33 @@ def test_gemm_mfma_ksplit_closed_forms():
     # a split that does not divide the k-steps is no split
     assert np.array_equal(oracle.emu_gemm_mfma(x, np.eye(128, dtype=np.float32), "BF16X9",
                                                ksplit=3), x)
+
+
+# ------------------------------------------------------------ rule search
+
+def test_search_model_default_is_the_oracle():
+    """tests/mfma_search.py restates the matrix-unit rules as a parameterised
+    model in plain Python integers (code of its own).  Its default
+    parameters must give the oracle's result bit for bit on every family of
+    random instruction pairs, and every alternative of its list must differ
+    from the oracle on some of them (otherwise the GPU search could not tell
+    it apart)."""
+    import mfma_search as ms
+    from mfma_families import FAMILIES, family
+
+    wrong = {name: 0 for name, _ in ms.ALTERNATIVES}
+    for fi, fam in enumerate(FAMILIES):
+        rng = np.random.default_rng(100 + fi)
+        a, b = family(fam, rng, 24, 24)
+        ab, bb = _bits(a), _bits(b)
+        ia, jb = np.repeat(np.arange(24), 24), np.tile(np.arange(24), 24)
+        acc1 = oracle.mfma_bf16_dot16(np.zeros(ia.size, np.float32), ab[ia, :16], bb[:16, jb].T)
+        want = oracle.mfma_bf16_dot16(acc1, ab[ia, 16:], bb[16:, jb].T).view(np.uint32)
+        got = np.array([ms.instruction_pair(ab[i], bb[:, j], ms.DEFAULT) for i, j in zip(ia, jb)],
+                       np.float32).view(np.uint32)
+        assert np.array_equal(got, want), f"{fam}: default rules differ from the oracle"
+        for name, r in ms.ALTERNATIVES:
+            alt = np.array([ms.instruction_pair(ab[i], bb[:, j], r) for i, j in zip(ia, jb)],
+                           np.float32).view(np.uint32)
+            wrong[name] += int((alt != want).sum())
+    assert all(v > 0 for v in wrong.values()), f"alternatives the families cannot tell apart: {wrong}"
