@@ -25,6 +25,15 @@ spin, median of 5 runs of 20 calls).
     python3 -m emulated_fp32_matrix_amd.policies [--stacks 2 3 4] [--json out.json]
     python3 -m emulated_fp32_matrix_amd.policies --ksplit-sweep --stacks 2 4 [--json out.json]
     python3 -m emulated_fp32_matrix_amd.policies --markdown out.json   # tables of a saved run
+
+With --launches it runs each stack's 8 GEMMs in AUTO and in NATIVE_F32,
+queued behind a GPU spin (so that the kernels run back to back), five times:
+the run to profile with `rocprofv3 --kernel-trace`.  --launch-table
+summarises that trace per kind of kernel and per stack.
+
+    rocprofv3 --kernel-trace -d DIR -o kt --output-format csv -- \
+        python3 -m emulated_fp32_matrix_amd.policies --launches --stacks 2 4
+    python3 -m emulated_fp32_matrix_amd.policies --launch-table DIR/kt_kernel_trace.csv --stacks 2 4
 """
 from __future__ import annotations
 
@@ -164,6 +173,93 @@ def ksplit_sweep(stack):
     return {"stack": stack, "name": synth.CONFIG_NAMES[stack], "gemms": rows}
 
 
+LAUNCH_REPS = 5
+
+
+def launches(stacks):
+    """The kernel sequence --launch-table reads: per stack and mode
+    (AUTO, NATIVE_F32), LAUNCH_REPS repetitions of the 8 GEMMs, each queued
+    behind a GPU spin."""
+    import torch
+
+    import emulated_fp32_matrix_amd as emu
+
+    synth = _synth()
+    dev = torch.device("cuda:0")
+    for stack in stacks:
+        gemms = synth.gemms(stack)
+        tensors = [(g, torch.from_numpy(synth.make_a(g)).to(dev), torch.from_numpy(synth.make_b(g)).to(dev),
+                    torch.empty((g.M, g.N), dtype=torch.float32, device=dev)) for g in gemms]
+        for mode in ("AUTO", "NATIVE_F32"):
+            for _ in range(LAUNCH_REPS):
+                torch.cuda.synchronize()
+                torch.cuda._sleep(20_000_000)
+                for g, a, b, c in tensors:
+                    emu.sgemm(a, b, mode=mode, trans_a=g.trans_a, trans_b=g.trans_b, c=c)
+            torch.cuda.synchronize()
+            print(f"stack {stack} {mode}: {LAUNCH_REPS} queued runs", flush=True)
+        del tensors
+        torch.cuda.empty_cache()
+
+
+def _kernel_kind(name):
+    for key, kind in (("presplit_kernel", "B pre-split"), ("pack_b_f32", "B pack (native)"),
+                      ("ksplit_reduce", "K-split reduction"), ("gemm_bf16", "emulated GEMM"),
+                      ("gemm_f32", "native GEMM")):
+        if key in name:
+            return kind
+    return None
+
+
+def launch_table(trace_csv, stacks):
+    """Markdown summary of a kernel trace of launches(): per stack and mode,
+    the median over the repetitions of the summed device time of each kind
+    of kernel (start to end of each launch), the number of launches, and the
+    span of the 8 GEMMs from the first launch's start to the last one's
+    end."""
+    import csv
+
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    runs, cur = [], None
+    for r in rows:
+        name = r["Kernel_Name"]
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        if "spin_kernel" in name:
+            cur = []
+            runs.append(cur)
+        elif cur is not None:
+            cur.append((name, t0, t1))
+    expect = len(stacks) * 2 * LAUNCH_REPS
+    assert len(runs) == expect, f"{len(runs)} queued runs in the trace, expected {expect}"
+    synth = _synth()
+    out = ["| stack | mode | launches per step | " + " | ".join(
+        ["B pre-split us", "B pack us", "K-split reduction us", "GEMM kernels us"]) +
+        " | step span us |", "|---|---|---|---|---|---|---|---|"]
+    i = 0
+    for stack in stacks:
+        for mode in ("AUTO", "NATIVE_F32"):
+            sums = {}
+            spans, counts = [], []
+            for run in runs[i:i + LAUNCH_REPS]:
+                per = {}
+                for name, t0, t1 in run:
+                    kind = _kernel_kind(name)
+                    if kind in ("emulated GEMM", "native GEMM"):
+                        kind = "GEMM kernels"
+                    if kind is not None:
+                        per[kind] = per.get(kind, 0.0) + (t1 - t0) / 1e3
+                for k, v in per.items():
+                    sums.setdefault(k, []).append(v)
+                spans.append((run[-1][2] - run[0][1]) / 1e3)
+                counts.append(len(run))
+            i += LAUNCH_REPS
+            cell = lambda k: f"{statistics.median(sums[k]):.1f}" if k in sums else ""
+            out.append(f"| {synth.CONFIG_NAMES[stack]} | {mode} | {statistics.median(counts):.0f} | "
+                       f"{cell('B pre-split')} | {cell('B pack (native)')} | {cell('K-split reduction')} | "
+                       f"{cell('GEMM kernels')} | {statistics.median(spans):.1f} |")
+    return "\n".join(out)
+
+
 def _policy_markdown(res):
     out = []
     for r in res:
@@ -227,7 +323,15 @@ def main():
     ap.add_argument("--json", default=None)
     ap.add_argument("--ksplit-sweep", action="store_true")
     ap.add_argument("--markdown", default=None, help="print the tables of a JSON file written earlier")
+    ap.add_argument("--launches", action="store_true", help="queued stack runs for a kernel trace")
+    ap.add_argument("--launch-table", default=None, help="summarise a kernel trace of --launches")
     args = ap.parse_args()
+    if args.launch_table:
+        print(launch_table(args.launch_table, args.stacks))
+        return
+    if args.launches:
+        launches(args.stacks)
+        return
     if args.markdown:
         res = json.load(open(args.markdown))
         print(_ksplit_markdown(res) if res and "gemms" in res[0] else _policy_markdown(res))
