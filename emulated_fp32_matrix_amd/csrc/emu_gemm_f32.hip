@@ -53,15 +53,18 @@ __device__ __forceinline__ int tile_k(int t)
     return KC ? ((t & 7) * 4) : ((t / RPP) * 4);
 }
 
-template <bool KC, int ROWS, int RPP>
+// WIDE: 64-bit per-lane offsets, for a tile whose rows (or k rows) span
+// 2^31 elements or more.
+template <bool KC, bool WIDE, int ROWS, int RPP>
 __device__ __forceinline__ void load_tile(RegTile<ROWS, RPP>& rt, const float* __restrict__ X,
                                           int64_t ld, int64_t rows, int64_t K, int64_t row0,
                                           int64_t k0, bool vec)
 {
+    typedef typename std::conditional<WIDE, int64_t, uint32_t>::type off_t;
     const int t = threadIdx.x;
     const int kk = tile_k<KC, RPP>(t);
     const int64_t gk = k0 + kk;
-    // Uniform tile base plus a 32-bit per-lane offset.
+    // Uniform tile base plus a per-lane offset (32-bit unless WIDE).
     const float* base = KC ? X + row0 * ld + k0 : X + k0 * ld + row0;
     const bool interior = row0 + ROWS <= rows && k0 + BK <= K;
 #pragma unroll
@@ -69,7 +72,7 @@ __device__ __forceinline__ void load_tile(RegTile<ROWS, RPP>& rt, const float* _
         const int r = tile_row<KC, RPP>(t, q);
         const int64_t gr = row0 + r;
         if (KC) {
-            const uint32_t off = (uint32_t)(r * ld + kk);
+            const off_t off = (off_t)(r * ld + kk);
             if (vec && (interior || (gr < rows && gk + 3 < K))) {
                 const f32x4_t v = *reinterpret_cast<const f32x4_t*>(base + off);
                 rt.v[q][0] = v[0];
@@ -84,7 +87,7 @@ __device__ __forceinline__ void load_tile(RegTile<ROWS, RPP>& rt, const float* _
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t off = (uint32_t)((kk + e) * ld + r);
+                const off_t off = (off_t)((kk + e) * ld + r);
                 rt.v[q][e] = (interior || (gr < rows && gk + e < K)) ? base[off] : 0.0f;
             }
         }
@@ -117,7 +120,7 @@ __device__ __forceinline__ void tile_coords(const Params& p, int pos, int bm, in
 // (lane / 32) feeds the k values h*16 .. h*16+15 of a BK step to successive
 // v_mfma_f32_32x32x2_f32 instructions (A and B use the same k order, so every
 // product a(i,k) b(k,j) is formed exactly once).
-template <class GEO, bool TA, bool TB>
+template <class GEO, bool TA, bool TB, bool WIDE>
 __global__ __launch_bounds__(GEO::NT, 2) void gemm_f32_kernel(Params p)
 {
     constexpr int BM = GEO::BM, BN = GEO::BN, TM = GEO::TM, TN = GEO::TN, RPP = GEO::RPP;
@@ -149,8 +152,8 @@ __global__ __launch_bounds__(GEO::NT, 2) void gemm_f32_kernel(Params p)
         int64_t m0, n0;
         tile_coords(p, slot + tl * G, BM, BN, m0, n0);
         const int64_t k0 = (int64_t)kt * BK;
-        load_tile<!TA>(ra, p.A, p.lda, p.M, p.K, m0, k0, p.vec_a);
-        load_tile<TB>(rb, p.B, p.ldb, p.N, p.K, n0, k0, p.vec_b);
+        load_tile<!TA, WIDE>(ra, p.A, p.lda, p.M, p.K, m0, k0, p.vec_a);
+        load_tile<TB, WIDE>(rb, p.B, p.ldb, p.N, p.K, n0, k0, p.vec_b);
     };
 
     prefetch(0);
@@ -600,19 +603,40 @@ Params make_params(const GemmArgs& g, int bm, int bn)
     return p;
 }
 
-// Tile counts and per-tile offsets must fit the kernels' 32-bit arithmetic:
-// tiles x k-steps < 2^31, and a tile's rows (or k rows) span < 2^31 elements.
-bool fits_32bit(const GemmArgs& g, int bm, int bn)
+using GeoF32Staged = Geo<2, 2, 2, 2>;   // 4 waves, each 64x64: 128x128 per workgroup
+
+// Tile counts must fit the kernel's 32-bit arithmetic (tiles x k-steps <
+// 2^31); per-tile offsets need the WIDE kernel when a tile's rows (or k
+// rows) span 2^31 elements or more.
+bool tiles_fit_32bit(const GemmArgs& g, int bm, int bn)
 {
     const int64_t tiles = ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
     const int64_t nk = (g.K + BK - 1) / BK;
+    return tiles * nk < ((int64_t)1 << 31);
+}
+
+bool needs_wide_offsets(const GemmArgs& g, int bm, int bn)
+{
     const int64_t lim = (int64_t)1 << 31;
     const int64_t span_a = (g.trans_a ? (int64_t)BK : (int64_t)bm) * g.lda;
     const int64_t span_b = (g.trans_b ? (int64_t)bn : (int64_t)BK) * g.ldb;
-    return tiles * nk < lim && span_a < lim && span_b < lim;
+    return span_a >= lim || span_b >= lim;
 }
 
-using GeoF32 = Geo<2, 2, 2, 2>;     // 4 waves, each 64x64: 128x128 per workgroup
+template <bool WIDE>
+void launch_f32_staged(const Params& p, bool ta, bool tb, int grid, hipStream_t stream)
+{
+    constexpr int NT = GeoF32Staged::NT;
+    if (!ta && !tb)
+        hipLaunchKernelGGL((gemm_f32_kernel<GeoF32Staged, false, false, WIDE>), dim3(grid), dim3(NT), 0, stream, p);
+    else if (!ta && tb)
+        hipLaunchKernelGGL((gemm_f32_kernel<GeoF32Staged, false, true, WIDE>), dim3(grid), dim3(NT), 0, stream, p);
+    else if (ta && !tb)
+        hipLaunchKernelGGL((gemm_f32_kernel<GeoF32Staged, true, false, WIDE>), dim3(grid), dim3(NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_f32_kernel<GeoF32Staged, true, true, WIDE>), dim3(grid), dim3(NT), 0, stream, p);
+}
+
 
 }  // namespace
 
@@ -661,19 +685,14 @@ hipError_t launch_gemm_native_f32(const GemmArgs& g, const DeviceInfo& dev, void
         hipLaunchKernelGGL(gemm_f32_pp_kernel, dim3(grid), dim3(512), 0, stream, p, W);
         return hipGetLastError();
     }
-    if (!fits_32bit(g, GeoF32::BM, GeoF32::BN)) return hipErrorInvalidValue;
-    const Params p = make_params(g, GeoF32::BM, GeoF32::BN);
+    if (!tiles_fit_32bit(g, GeoF32Staged::BM, GeoF32Staged::BN)) return hipErrorInvalidValue;
+    const Params p = make_params(g, GeoF32Staged::BM, GeoF32Staged::BN);
     const int cap = 2 * dev.num_cu;
     const int grid = p.ntiles < cap ? p.ntiles : cap;
-    constexpr int NT = GeoF32::NT;
-    if (!g.trans_a && !g.trans_b)
-        hipLaunchKernelGGL((gemm_f32_kernel<GeoF32, false, false>), dim3(grid), dim3(NT), 0, stream, p);
-    else if (!g.trans_a && g.trans_b)
-        hipLaunchKernelGGL((gemm_f32_kernel<GeoF32, false, true>), dim3(grid), dim3(NT), 0, stream, p);
-    else if (g.trans_a && !g.trans_b)
-        hipLaunchKernelGGL((gemm_f32_kernel<GeoF32, true, false>), dim3(grid), dim3(NT), 0, stream, p);
+    if (needs_wide_offsets(g, GeoF32Staged::BM, GeoF32Staged::BN))
+        launch_f32_staged<true>(p, g.trans_a, g.trans_b, grid, stream);
     else
-        hipLaunchKernelGGL((gemm_f32_kernel<GeoF32, true, true>), dim3(grid), dim3(NT), 0, stream, p);
+        launch_f32_staged<false>(p, g.trans_a, g.trans_b, grid, stream);
     return hipGetLastError();
 }
 

@@ -408,3 +408,54 @@ def test_native_kernels_agree_bitwise(tb):
                 outs.append(cd.cpu().numpy())
         assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3]), (M, N, K, tb)
         check_result(outs[0], oracle.gemm_f64(a, b_op), a, b_op, "NATIVE_F32", label=f"native {M}x{N}x{K}")
+
+
+# ------------------------------------------------- leading dimensions past 2^31
+
+BIG_LD = (1 << 24) + 64   # a 128-row tile of A (or 32 k-rows of B) spans more than 2^31 elements
+
+
+@pytest.mark.parametrize("mode", list(MODES) + ["AUTO"])
+@pytest.mark.parametrize("which", ["lda", "ldb_t", "ldc"])
+def test_leading_dimensions_past_32bit_offsets(which, mode):
+    """Huge leading dimensions (a tile of A, or of op(B) stored transposed,
+    spanning more than 2^31 elements; or C rows 2^26 bytes apart): tiny
+    shapes over 67 MB buffers.  Such A takes the pre-split path of the
+    emulated modes and the 64-bit-offset staged kernel of NATIVE_F32, C the
+    element-wise stores; the result equals the same product on compact
+    operands bit for bit and the FP64 oracle within its bound."""
+    import torch
+
+    import emulated_fp32_matrix_amd as emu
+
+    dev = torch.device("cuda:0")
+    M, N, K = 3, 40, 72
+    rng = np.random.default_rng(11)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    bop = rng.standard_normal((K, N)).astype(np.float32)
+    tb = which == "ldb_t"
+    say(f"leading dimension {which} = {BIG_LD}, {mode}")
+    ga = torch.from_numpy(a).to(dev)
+    gb = torch.from_numpy(np.ascontiguousarray(bop.T) if tb else bop).to(dev)
+    want = emu.sgemm(ga, gb, mode=mode, trans_b=tb)
+    if which == "lda":
+        buf = torch.zeros((M - 1) * BIG_LD + K, device=dev)
+        ga = buf.as_strided((M, K), (BIG_LD, 1))
+        ga.copy_(torch.from_numpy(a).to(dev))
+    elif which == "ldb_t":
+        buf = torch.zeros((N - 1) * BIG_LD + K, device=dev)
+        gb = buf.as_strided((N, K), (BIG_LD, 1))
+        gb.copy_(torch.from_numpy(np.ascontiguousarray(bop.T)).to(dev))
+    c = None
+    if which == "ldc":
+        cbuf = torch.full(((M - 1) * (BIG_LD + 32) + N,), float("nan"), device=dev)
+        c = cbuf.as_strided((M, N), (BIG_LD + 32, 1))
+    got = emu.sgemm(ga, gb, mode=mode, trans_b=tb, c=c)
+    torch.cuda.synchronize()
+    got, want = got.cpu().numpy(), want.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"{which} {mode}: differs from compact"
+    run_mode = emu.select_mode(M, N, K, False, tb) if mode == "AUTO" else mode
+    check_result(got, oracle.gemm_f64(a, bop), a, bop, run_mode, label=f"{which} {mode}")
+    if which == "ldc":   # nothing outside C's rows and columns written
+        gap = cbuf.as_strided((M - 1, BIG_LD + 32 - N), (BIG_LD + 32, 1), N).cpu().numpy()
+        assert np.isnan(gap).all()
