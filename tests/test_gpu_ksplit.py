@@ -128,14 +128,16 @@ def test_auto_policy_on_the_small_stacks(cfg):
 
 
 @pytest.mark.parametrize("mode", ["BF16X9", "BF16X6", "BF16X3", "BF16X1"])
-@pytest.mark.parametrize("M,N,K,tb", [(3300, 1200, 512, False), (3300, 1199, 512, True)])
+@pytest.mark.parametrize("M,N,K,tb", [(3300, 1200, 512, False), (3300, 1199, 512, True),
+                                      (4489, 1030, 1024, False)])
 def test_last_round_split_bitwise(mode, M, N, K, tb):
     """EMU_KSPLIT_AUTO on shapes whose plan splits only the last round of
-    tiles (256 whole tiles, then 4 split ones, the first split tile inside a
-    row of tiles; M and N ragged; N a multiple of 4 or not: vector or
-    element-wise reduction; NN and NT): with alpha, beta and a bias, whole
-    tiles equal the model without a split, split tiles the model at ksplit
-    S, bit for bit."""
+    tiles (128-row tiles: 256 whole tiles, then 4 split ones; 64-row tiles:
+    512 whole, then 127 split; the first split tile inside a row of tiles;
+    M and N ragged; N a multiple of 4 or not: vector or element-wise
+    reduction; NN and NT): with alpha, beta and a bias, whole tiles equal
+    the model without a split, split tiles the model at ksplit S, bit for
+    bit."""
     import emulated_fp32_matrix_amd as emu
 
     plan = emu.select_plan(M, N, K)
