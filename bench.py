@@ -52,6 +52,8 @@ def parse():
                     help="skip the NATIVE_F32 and torch-fp32 context timings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock reading after the timed region")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy 1 GiB three times with one elementwise kernel "
                          "(the reference that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -73,14 +75,6 @@ TRAFFIC_BY_SOURCE = {
 }
 
 
-# Shader clock of the main BF16X9 kernel over this workload (GHz), from a
-# rocprofv3 pass with GRBM_GUI_ACTIVE (GPU-busy cycles at the shader clock,
-# summed over the 8 XCDs) and the kernel trace of the same dispatches:
-# sum(GRBM_GUI_ACTIVE / 8) / sum(duration) over the launches of the timed steps.
-# Keyed like TRAFFIC_BY_SOURCE; a changed kernel reports null.
-SCLK_BY_SOURCE = {
-    "bdcdf111e991602f3f57b8fcd0c2018b43080069b1718fe08138c2bc7f79b813": 1.735,
-}
 SPEC_SCLK_GHZ = 2.4         # the clock of the spec peaks
 
 
@@ -104,6 +98,84 @@ def kernel_source_hash():
         with open(os.path.join(_ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def _smi_handle(amdsmi, torch):
+    """The amdsmi handle of torch's current device (matched by PCI address;
+    amdsmi lists every GPU of the machine, whatever the visible devices)."""
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+    handles = amdsmi.amdsmi_get_processor_handles()
+    for h in handles:
+        dom, bus, rest = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")
+        if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+            return h
+    return handles[0] if len(handles) == 1 else None
+
+
+def clock_under_load(torch, emu, gemms, tensors, mode, max_s=4.0):
+    """Shader clock of the same steps as the timed region, run again right
+    after it.  The driver's GPU metrics table (read through amdsmi) refreshes
+    about once a second with each XCD's clock, the socket power and the GFX
+    activity over the interval since the previous refresh; the steps keep
+    the GPU busy until an interval that began after they started has been
+    reported fully busy, and that reading is returned (None when amdsmi is
+    missing or gives no such interval within max_s seconds)."""
+    try:
+        import amdsmi
+    except ImportError:
+        return None
+    try:
+        amdsmi.amdsmi_init()
+    except Exception as e:   # noqa: BLE001 - the reading is optional
+        log(f"clock reading: amdsmi_init failed ({e})")
+        return None
+    try:
+        handle = _smi_handle(amdsmi, torch)
+        if handle is None:
+            return None
+
+        def read():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            return (m.get("accumulation_counter"), m.get("current_gfxclks"), m.get("current_socket_power"),
+                    m.get("average_gfx_activity"))
+
+        stream = torch.cuda.current_stream()
+        last = read()[0]
+        refreshes = 0
+        done = None
+        prev = None
+        t0 = time.perf_counter()
+        while done is None and time.perf_counter() - t0 < max_s:
+            for _ in range(8):
+                for g, (a, b, c) in zip(gemms, tensors):
+                    emu.sgemm(a, b, mode=mode, trans_a=g.trans_a, trans_b=g.trans_b, c=c, stream=stream)
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            if prev is not None:
+                prev.synchronize()   # one batch of steps stays queued behind the one running
+            prev = ev
+            acc, clks, power, busy = read()
+            if acc == last:
+                continue
+            last = acc
+            refreshes += 1
+            # the first refresh's interval began before the steps did
+            if refreshes >= 2 and isinstance(busy, (int, float)) and busy >= 95:
+                mhz = [float(x) for x in clks if isinstance(x, (int, float))]
+                if mhz:
+                    done = {"sclk_ghz": round(sum(mhz) / len(mhz) / 1e3, 3),
+                            "xcd_ghz": [round(x / 1e3, 3) for x in mhz],
+                            "socket_power_w": power, "gfx_activity_pct": busy,
+                            "after_s": round(time.perf_counter() - t0, 2)}
+        torch.cuda.synchronize()
+        return done
+    except Exception as e:   # noqa: BLE001
+        log(f"clock reading failed ({e})")
+        torch.cuda.synchronize()
+        return None
+    finally:
+        amdsmi.amdsmi_shut_down()
 
 
 def make_inputs(torch, dev, gemms):
@@ -246,17 +318,22 @@ def main():
     avg_us = float(per.sum()) / n_launch * 1e3
     peak = BF16_PEAK_TFLOPS if mode in BANDS else F32_PEAK_TFLOPS
     achieved = P * float(flops.sum()) / n_launch / (avg_us * 1e-6) / 1e12
-    traffic = sclk = None
+    traffic = None
     if mode == "BF16X9":
-        src = kernel_source_hash()
-        traffic = TRAFFIC_BY_SOURCE.get(src)
-        sclk = SCLK_BY_SOURCE.get(src)
+        traffic = TRAFFIC_BY_SOURCE.get(kernel_source_hash())
+    clock = None if args.no_clock else clock_under_load(torch, emu, gemms, tensors, mode)
+    sclk = clock["sclk_ghz"] if clock else None
+    if clock:
+        log(f"clock under load: {clock}")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
-                # the same fraction against the peak at the clock the kernel ran at
+                # the same fraction against the peak at the clock the steps run at
                 "sclk_ghz": sclk,
                 "frac_at_measured_clock": (round(achieved / (peak * sclk / SPEC_SCLK_GHZ), 4)
                                            if sclk else None),
+                "clock": ({"source": "amdsmi GPU metrics: mean of the XCD clocks over a fully busy "
+                                     "1 s interval of the same steps, right after the timed region",
+                           **clock} if clock else None),
                 "kernel": ("gemm_bf16_pp_kernel<%d, false, false, 128>" % BANDS[mode])
                 if mode in BANDS else "gemm_f32_pp_kernel",
                 "avg_launch_us": round(avg_us, 2),
