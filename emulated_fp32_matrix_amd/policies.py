@@ -9,11 +9,18 @@ Interatomic Potentials" (section "BF16x9 on NVIDIA Blackwell GPUs"):
 once beforehand (emu_presplit_b) and used by emu_sgemm_presplit, as a fixed
 model in inference or molecular dynamics allows.
 
-Per stack and policy it reports the step time two ways:
+Per stack and policy it reports the step time three ways:
   wall   - HIP events around the 8 calls issued back to back, what a caller
            that launches eagerly from Python sees (host launch cost included);
   device - the same 8 calls queued behind a GPU spin, so the events time the
-           device work alone (what a captured graph or a busy stream sees).
+           device work alone (what a captured graph or a busy stream sees);
+  steady - the 8 calls repeated back to back for about half a second, timed
+           over the second half: the sustained rate of a training or
+           molecular-dynamics loop.  The two one-shot figures start from a
+           GPU that was idle or spinning, whose clock has not settled under
+           the load yet (it first comes up, and on the power-limited shapes
+           then falls back to what the power limit allows); the native path,
+           which runs near the spec clock once settled, loses most there.
 
 With --ksplit-sweep it instead times every GEMM of the stacks in BF16X9
 with each K split S of every tile (a divisor of ceil(K/32), S <= 8;
@@ -106,11 +113,24 @@ def time_stack(stack, reps=5):
                 torch.cuda.synchronize()
                 (devs if gated else walls).append(e0.elapsed_time(e1) * 1e3)
         w, d = statistics.median(walls), statistics.median(devs)
+        # steady: about half a second of steps back to back, the second half timed
+        n = max(20, int(0.5e6 / d))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for i in range(n):
+            step(mode)
+            if i == n // 2:
+                ev[0].record(stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        st = ev[0].elapsed_time(ev[1]) * 1e3 / (n - n // 2 - 1)
         out["policies"][pol] = {"mode": mode, "wall_us": round(w, 1), "device_us": round(d, 1),
+                                "steady_us": round(st, 1),
                                 "wall_tflops": round(flops / w / 1e6, 2),
-                                "device_tflops": round(flops / d / 1e6, 2)}
+                                "device_tflops": round(flops / d / 1e6, 2),
+                                "steady_tflops": round(flops / st / 1e6, 2)}
         print(f"stack {stack} {pol:10s} ({mode:10s}): wall {w:9.1f} us ({flops / w / 1e6:6.1f} TFLOP/s)  "
-              f"device {d:9.1f} us ({flops / d / 1e6:6.1f} TFLOP/s)", flush=True)
+              f"device {d:9.1f} us ({flops / d / 1e6:6.1f} TFLOP/s)  steady {st:9.1f} us "
+              f"({flops / st / 1e6:6.1f} TFLOP/s)", flush=True)
     del tensors
     torch.cuda.empty_cache()
     return out
@@ -269,12 +289,14 @@ def _policy_markdown(res):
                            for k, v in r["auto_choice"].items())
         out.append(f"AUTO's choices: {choice}\n")
         out.append("| policy | mode | wall us | wall TFLOP/s | wall speedup | device us | device TFLOP/s "
-                   "| device speedup |\n|---|---|---|---|---|---|---|---|")
+                   "| device speedup | steady us | steady TFLOP/s | steady speedup |\n"
+                   "|---|---|---|---|---|---|---|---|---|---|---|")
         nat = r["policies"]["native"]
         for name, p in r["policies"].items():
             out.append(f"| {name} | {p['mode']} | {p['wall_us']:.1f} | {p['wall_tflops']:.1f} | "
                        f"{nat['wall_us'] / p['wall_us']:.2f} | {p['device_us']:.1f} | "
-                       f"{p['device_tflops']:.1f} | {nat['device_us'] / p['device_us']:.2f} |")
+                       f"{p['device_tflops']:.1f} | {nat['device_us'] / p['device_us']:.2f} | "
+                       f"{p['steady_us']:.1f} | {p['steady_tflops']:.1f} | {nat['steady_us'] / p['steady_us']:.2f} |")
         out.append("")
     return "\n".join(out)
 

@@ -43,7 +43,11 @@
  *     creating one fails); growing frees the old buffer with hipFreeAsync on
  *     the stream.  Up to 16 streams per device keep a buffer; beyond that the
  *     least recently used one is released with hipFree, which waits for the
- *     device.  The buffers live until the process ends.  emu_split_bf16x3
+ *     device.  The buffers live until the process ends.  A call whose stream
+ *     already holds a buffer as large as the call needs allocates nothing
+ *     and issues only kernel launches, so it can be captured in a HIP graph
+ *     on that stream: run the same calls on the stream once before the
+ *     capture (emu_sgemm_noalloc needs no such run).  emu_split_bf16x3
  *     allocates nothing, and emu_sgemm_noalloc works in a fixed scratch
  *     instead of a stream's buffer.  The cache knows streams only by their handle:
  *     synchronise a stream that ran library calls before destroying it, so
