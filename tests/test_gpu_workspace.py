@@ -78,3 +78,60 @@ def test_more_streams_than_kept_buffers():
         torch.cuda.synchronize()
         for o in outs:
             assert np.array_equal(o.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_host_threads_each_on_its_own_stream():
+    """Four host threads, each on a stream of its own, issue 12 calls each at
+    the same time (the binding releases the GIL in the library call): mixed
+    modes and shapes whose workspaces grow call after call, K splits,
+    NATIVE_F32's packed B.  Every result equals the same call made alone
+    from one thread."""
+    import threading
+
+    import torch
+
+    import emulated_fp32_matrix_amd as emu
+
+    plans = []
+    for t in range(4):
+        rng = np.random.default_rng(100 + t)
+        calls = []
+        for i in range(12):
+            M, N = int(rng.integers(64, 1500)), int(rng.integers(32, 1200))
+            K = int(rng.integers(8, 300)) * 4
+            mode = ["BF16X9", "BF16X6", "AUTO", "NATIVE_F32", "BF16X3"][(t + i) % 5]
+            nk = -(-K // 32)
+            ksplit = 2 if mode in ("BF16X9", "BF16X6") and nk % 2 == 0 and i % 3 == 0 else None
+            a = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).cuda()
+            b = torch.from_numpy(rng.standard_normal((K, N)).astype(np.float32)).cuda()
+            calls.append((a, b, mode, ksplit))
+        plans.append(calls)
+    alone = [[emu.sgemm(a, b, mode=m, ksplit=s).cpu() for a, b, m, s in calls] for calls in plans]
+    torch.cuda.synchronize()
+
+    results = [None] * 4
+    errors = []
+
+    def worker(t):
+        try:
+            st = torch.cuda.Stream()
+            outs = []
+            with torch.cuda.stream(st):
+                for a, b, m, s in plans[t]:
+                    outs.append(emu.sgemm(a, b, mode=m, ksplit=s))
+            st.synchronize()
+            results[t] = [o.cpu() for o in outs]
+        except Exception as e:   # reported by the main thread
+            errors.append((t, repr(e)))
+
+    for _ in range(2):
+        threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join(timeout=120)
+        assert not any(th.is_alive() for th in threads), "a thread did not finish"
+        assert not errors, errors
+        for t in range(4):
+            for i, (o, want) in enumerate(zip(results[t], alone[t])):
+                assert torch.equal(o.view(torch.int32), want.view(torch.int32)), (t, i, plans[t][i][2])
