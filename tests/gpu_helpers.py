@@ -1,5 +1,5 @@
 """Shared helpers of the GPU parity tests: run a GEMM through the C ABI and
-judge it against the CPU oracle.
+check it against the CPU oracle.
 
 Pass rules (the emulation's accuracy contract):
   * normwise: err_F = ||C - C_ref||_F / ||C_ref||_F against the FP64 oracle,
