@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-clock", action="store_true",
-                    help="skip the shader-clock reading after the timed region")
+                    help="skip the shader-clock reading and the matrix-unit stream after the timed region")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy 1 GiB three times with one elementwise kernel "
                          "(the reference that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -176,6 +176,22 @@ def clock_under_load(torch, emu, gemms, tensors, mode, max_s=4.0):
         return None
     finally:
         amdsmi.amdsmi_shut_down()
+
+
+def mfma_stream_rate(kind):
+    """The matrix units' sustained rate on this device under a dense stream
+    of the same matrix instruction (emulated_fp32_matrix_amd.ceiling: every
+    SIMD, register operands, about 1 s): the practical roof the kernel's
+    rate is set against.  None when the probe library is not built."""
+    try:
+        from emulated_fp32_matrix_amd import ceiling
+
+        r = ceiling.run(kind, 1.0)
+    except Exception as e:   # noqa: BLE001 - the reading is optional
+        log(f"matrix-unit stream: not measured ({e})")
+        return None
+    return {"instruction": r["instruction"], "tflops": r["tflops"], "sclk_ghz": r["sclk_ghz"],
+            "frac_of_spec": r["frac_of_spec"]}
 
 
 def make_inputs(torch, dev, gemms):
@@ -325,6 +341,9 @@ def main():
     sclk = clock["sclk_ghz"] if clock else None
     if clock:
         log(f"clock under load: {clock}")
+    stream = None if args.no_clock else mfma_stream_rate("bf16" if mode in BANDS else "f32")
+    if stream:
+        log(f"matrix-unit stream: {stream}")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 # the same fraction against the peak at the clock the steps run at
@@ -334,6 +353,10 @@ def main():
                 "clock": ({"source": "amdsmi GPU metrics: mean of the XCD clocks over a fully busy "
                                      "1 s interval of the same steps, right after the timed region",
                            **clock} if clock else None),
+                # the practical roof: a dense stream of the same matrix
+                # instruction alone, on this device, right after
+                "mfma_stream": stream,
+                "frac_of_mfma_stream": round(achieved / stream["tflops"], 4) if stream else None,
                 "kernel": ("gemm_bf16_pp_kernel<%d, false, false, 128>" % BANDS[mode])
                 if mode in BANDS else "gemm_f32_pp_kernel",
                 "avg_launch_us": round(avg_us, 2),
