@@ -8,7 +8,7 @@ prints one JSON line per instruction (bf16 32x32x16, FP32 32x32x2): the
 sustained TFLOP/s, its fraction of the spec peak, the shader clock measured
 inside the kernel, and the socket power and GFX activity that the driver's
 GPU metrics table reports for a one-second interval inside the run (amdsmi;
-null where it is not importable).  ``build()`` compiles the library next to
+null where it is not importable or sees more than one GPU).  ``build()`` compiles the library next to
 this file (``__graft_entry__.build()`` calls it).
 """
 from __future__ import annotations
@@ -54,18 +54,30 @@ def _lib():
 
 class _Power:
     """Polls the GPU metrics table while the stream runs and keeps the
-    first refresh whose interval began after the polling started."""
+    first refresh whose interval began after the polling started.  Only on
+    a machine where amdsmi sees one GPU (the one the stream runs on);
+    elsewhere the reading is left out."""
 
-    def __init__(self, device_index: int = 0):
+    def __init__(self):
         self.reading = None
         self._stop = False
+        self._smi = None
         try:
             import amdsmi
+        except ImportError:
+            return
+        try:
             amdsmi.amdsmi_init()
-            self._smi = amdsmi
-            self._h = amdsmi.amdsmi_get_processor_handles()[device_index]
         except Exception:   # noqa: BLE001 - the reading is optional
-            self._smi = None
+            return
+        try:
+            handles = amdsmi.amdsmi_get_processor_handles()
+        except Exception:   # noqa: BLE001
+            handles = []
+        if len(handles) != 1:
+            amdsmi.amdsmi_shut_down()
+            return
+        self._smi, self._h = amdsmi, handles[0]
 
     def _run(self):
         m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
